@@ -43,7 +43,7 @@ def _f64(x):
 
 
 def _prep(q, scale, rows, n):
-    d = q.shape[-1]
+    d = int(q.shape[-1])
     if scale is None or scale <= 0:
         scale = 1.0 / np.sqrt(d)
     if rows is None:
@@ -56,31 +56,33 @@ def masked_attention_jvp(q, k, v, dq, dk, dv, allowed, scale=None, rows=None,
                          row_block=512):
     """Masked attention and its tangent.
 
-    q, k, v, dq, dk, dv : array-like [B, N, H, D] (any float dtype)
+    q, k, v, dq, dk, dv : array-like [B, N, H, D] (numpy or torch, any float
+                          dtype); one (b, h) slice at a time is widened to fp64
     allowed : predicate object, ``allowed(rows) -> bool [len(rows), N]``
     rows    : query rows to evaluate (default: all N)
     returns (O, dO, LSE) as fp64: O, dO [B, R, H, D], LSE [B, H, R]
     """
-    q, k, v, dq, dk, dv = (_f64(x) for x in (q, k, v, dq, dk, dv))
     B, N, H, D = q.shape
     scale, rows = _prep(q, scale, rows, N)
     R = len(rows)
     O = np.zeros((B, R, H, D))
     dO = np.zeros((B, R, H, D))
     LSE = np.full((B, H, R), -np.inf)
+    blocks = []
     for r0 in range(0, R, row_block):
         rb = rows[r0:r0 + row_block]
         A = np.asarray(allowed(rb), dtype=bool)          # [r, N]
         cols = np.nonzero(A.any(axis=0))[0]
-        if cols.size == 0:
-            continue
-        A = A[:, cols]
-        live = A.any(axis=1)
-        for b in range(B):
-            for h in range(H):
-                qi, dqi = q[b, rb, h, :], dq[b, rb, h, :]
-                kj, vj = k[b, cols, h, :], v[b, cols, h, :]
-                dkj, dvj = dk[b, cols, h, :], dv[b, cols, h, :]
+        if cols.size:
+            blocks.append((r0, rb, cols, A[:, cols]))
+    for b in range(B):
+        for h in range(H):
+            qs, ks, vs = _f64(q[b, :, h, :]), _f64(k[b, :, h, :]), _f64(v[b, :, h, :])
+            dqs, dks, dvs = _f64(dq[b, :, h, :]), _f64(dk[b, :, h, :]), _f64(dv[b, :, h, :])
+            for r0, rb, cols, A in blocks:
+                live = A.any(axis=1)
+                qi, dqi = qs[rb], dqs[rb]
+                kj, vj, dkj, dvj = ks[cols], vs[cols], dks[cols], dvs[cols]
                 s = np.where(A, scale * (qi @ kj.T), -np.inf)
                 m = s.max(axis=1, keepdims=True)
                 m = np.where(np.isfinite(m), m, 0.0)
@@ -100,29 +102,30 @@ def masked_attention_jvp(q, k, v, dq, dk, dv, allowed, scale=None, rows=None,
 def masked_attention(q, k, v, allowed, scale=None, rows=None, row_block=512):
     """Primal only: (O, LSE) of the same masked operator (the first four
     lines of the definition in the module docstring)."""
-    q, k, v = (_f64(x) for x in (q, k, v))
     B, N, H, D = q.shape
     scale, rows = _prep(q, scale, rows, N)
     R = len(rows)
     O = np.zeros((B, R, H, D))
     LSE = np.full((B, H, R), -np.inf)
+    blocks = []
     for r0 in range(0, R, row_block):
         rb = rows[r0:r0 + row_block]
         A = np.asarray(allowed(rb), dtype=bool)
         cols = np.nonzero(A.any(axis=0))[0]
-        if cols.size == 0:
-            continue
-        A = A[:, cols]
-        live = A.any(axis=1)
-        for b in range(B):
-            for h in range(H):
-                s = np.where(A, scale * (q[b, rb, h, :] @ k[b, cols, h, :].T), -np.inf)
+        if cols.size:
+            blocks.append((r0, rb, cols, A[:, cols]))
+    for b in range(B):
+        for h in range(H):
+            qs, ks, vs = _f64(q[b, :, h, :]), _f64(k[b, :, h, :]), _f64(v[b, :, h, :])
+            for r0, rb, cols, A in blocks:
+                live = A.any(axis=1)
+                s = np.where(A, scale * (qs[rb] @ ks[cols].T), -np.inf)
                 m = s.max(axis=1, keepdims=True)
                 m = np.where(np.isfinite(m), m, 0.0)
                 e = np.where(A, np.exp(s - m), 0.0)
                 l = e.sum(axis=1, keepdims=True)
                 p = np.where(live[:, None], e / np.where(l > 0, l, 1.0), 0.0)
-                O[b, r0:r0 + len(rb), h, :] = p @ v[b, cols, h, :]
+                O[b, r0:r0 + len(rb), h, :] = p @ vs[cols]
                 LSE[b, h, r0:r0 + len(rb)] = np.where(
                     live, m[:, 0] + np.log(np.where(live, l[:, 0], 1.0)), -np.inf)
     return O, LSE
