@@ -1,1 +1,239 @@
-"""MI355X (gfx950) forward-mode JVP of masked scaled-dot-product attention."""
+"""MI355X (gfx950) forward-mode JVP of masked scaled-dot-product attention.
+
+Thin Python binding of ``libattn_jvp.so`` (C ABI in ``include/attn_jvp.h``).
+The functions carry the C names and only marshal arguments: every step of the
+computation runs in the library's HIP kernels on the GPU.  PyTorch supplies
+device memory and the current stream.
+
+    mask = attn_jvp_mask_tf(n_frames=21, tokens_per_frame=1560, frames_per_chunk=3)
+    o, d_o, lse = attn_jvp_fwd(q, k, v, dq, dk, dv, mask)   # [B, N, H, D] tensors
+"""
+
+import ctypes
+
+import numpy as np
+
+from . import _lib
+from ._lib import ATTN_JVP_BF16, ATTN_JVP_F32  # noqa: F401
+
+__all__ = [
+    "AttnJvpError", "Mask", "attn_jvp_mask_tf", "attn_jvp_mask_rects", "attn_jvp_mask_dense",
+    "attn_jvp_mask_info", "attn_jvp_mask_export", "attn_jvp_mask_schedule", "attn_jvp_mask_free",
+    "attn_jvp_fwd", "attn_jvp_tile_shape", "attn_jvp_status_str", "attn_jvp_version",
+]
+
+
+class AttnJvpError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {attn_jvp_status_str(status)} (status {status})")
+
+
+def _check(status, where):
+    if status != _lib.ATTN_JVP_OK:
+        raise AttnJvpError(status, where)
+
+
+def attn_jvp_status_str(status):
+    return _lib.lib().attn_jvp_status_str(int(status)).decode()
+
+
+def attn_jvp_version():
+    return _lib.lib().attn_jvp_version()
+
+
+class Mask:
+    """Owner of an ``attn_jvp_mask*``; freed with the object (or explicitly)."""
+
+    def __init__(self, handle):
+        self._h = ctypes.c_void_p(handle)
+
+    @property
+    def handle(self):
+        if not self._h.value:
+            raise ValueError("mask has been freed")
+        return self._h
+
+    def free(self):
+        if self._h.value:
+            _lib.lib().attn_jvp_mask_free(self._h)
+            self._h = ctypes.c_void_p(None)
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass
+
+    def info(self):
+        return attn_jvp_mask_info(self)
+
+
+def _new_mask(fn, *args):
+    out = ctypes.c_void_p()
+    st = fn(*args, ctypes.byref(out))
+    _check(st, fn.__name__)
+    return Mask(out.value)
+
+
+def attn_jvp_mask_tf(n_frames, tokens_per_frame, frames_per_chunk=1):
+    """Teacher-forcing mask over [clean | noisy] (see attn_jvp.h)."""
+    L = _lib.lib()
+    return _new_mask(L.attn_jvp_mask_tf, int(n_frames), int(tokens_per_frame),
+                     int(frames_per_chunk))
+
+
+def _i32arr(x):
+    a = np.ascontiguousarray(np.asarray(x, dtype=np.int32))
+    return a, a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def attn_jvp_mask_rects(n_q, n_k, group_q_begin, range_ptr, k_begin, k_end):
+    """Query groups with admissible key ranges in CSR form (see attn_jvp.h)."""
+    L = _lib.lib()
+    gq, gq_p = _i32arr(group_q_begin)
+    rp, rp_p = _i32arr(range_ptr)
+    kb, kb_p = _i32arr(k_begin)
+    ke, ke_p = _i32arr(k_end)
+    if len(rp) != len(gq) or len(kb) != len(ke):
+        raise ValueError("group_q_begin/range_ptr and k_begin/k_end lengths must match")
+    return _new_mask(L.attn_jvp_mask_rects, int(n_q), int(n_k), len(gq) - 1, gq_p, rp_p,
+                     kb_p if len(kb) else None, ke_p if len(ke) else None)
+
+
+def attn_jvp_mask_dense(n_q, n_k):
+    L = _lib.lib()
+    return _new_mask(L.attn_jvp_mask_dense, int(n_q), int(n_k))
+
+
+def attn_jvp_mask_info(mask):
+    """dict(n_q, n_k, n_groups, n_ranges, n_visible_pairs)."""
+    v = [ctypes.c_int32() for _ in range(4)]
+    nv = ctypes.c_int64()
+    _check(_lib.lib().attn_jvp_mask_info(mask.handle, *[ctypes.byref(x) for x in v],
+                                         ctypes.byref(nv)), "attn_jvp_mask_info")
+    return dict(n_q=v[0].value, n_k=v[1].value, n_groups=v[2].value, n_ranges=v[3].value,
+                n_visible_pairs=nv.value)
+
+
+def attn_jvp_mask_export(mask):
+    """Canonical CSR form: (group_q_begin, range_ptr, k_begin, k_end) int32 arrays."""
+    info = attn_jvp_mask_info(mask)
+    g, r = info["n_groups"], info["n_ranges"]
+    gq = np.zeros(g + 1, np.int32)
+    rp = np.zeros(g + 1, np.int32)
+    kb = np.zeros(max(r, 1), np.int32)
+    ke = np.zeros(max(r, 1), np.int32)
+    p = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    _check(_lib.lib().attn_jvp_mask_export(mask.handle, p(gq), p(rp), p(kb), p(ke)),
+           "attn_jvp_mask_export")
+    return gq, rp, kb[:r], ke[:r]
+
+
+def attn_jvp_mask_schedule(mask, block_m, block_n):
+    """Host copy of the kernels' block schedule for a tile shape (see attn_jvp.h)."""
+    L = _lib.lib()
+    nt, ne, npart = ctypes.c_int32(), ctypes.c_int64(), ctypes.c_int64()
+    _check(L.attn_jvp_mask_schedule(mask.handle, int(block_m), int(block_n), ctypes.byref(nt),
+                                    ctypes.byref(ne), ctypes.byref(npart), None, None, None,
+                                    None, None), "attn_jvp_mask_schedule")
+    words = block_n // 32
+    off = np.zeros(nt.value + 1, np.int32)
+    order = np.zeros(nt.value, np.int32)
+    eb = np.zeros(max(ne.value, 1), np.int32)
+    ep = np.zeros(max(ne.value, 1), np.int32)
+    bits = np.zeros(max(npart.value * block_m * words, 1), np.uint32)
+    p32 = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    _check(L.attn_jvp_mask_schedule(mask.handle, int(block_m), int(block_n), ctypes.byref(nt),
+                                    ctypes.byref(ne), ctypes.byref(npart), p32(off), p32(order),
+                                    p32(eb), p32(ep),
+                                    bits.ctypes.data_as(ctypes.POINTER(ctypes.c_uint32))),
+           "attn_jvp_mask_schedule")
+    n = ne.value
+    return dict(tile_offsets=off, tile_order=order, entry_block=eb[:n], entry_partial=ep[:n],
+                partial_bits=bits[:npart.value * block_m * words].reshape(
+                    npart.value, block_m, words))
+
+
+def attn_jvp_mask_free(mask):
+    mask.free()
+
+
+def attn_jvp_tile_shape(dtype, D):
+    bm, bn = ctypes.c_int32(), ctypes.c_int32()
+    _check(_lib.lib().attn_jvp_tile_shape(int(dtype), int(D), ctypes.byref(bm), ctypes.byref(bn)),
+           "attn_jvp_tile_shape")
+    return bm.value, bn.value
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return _lib.ATTN_JVP_BF16
+    if t.dtype == torch.float32:
+        return _lib.ATTN_JVP_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def attn_jvp_fwd(q, k, v, dq, dk, dv, mask, scale=None, o=None, d_o=None, lse=None,
+                 stream=None):
+    """Masked attention O, its tangent dO and the row log-sum-exp, in one pass.
+
+    q, dq: [B, n_q, H, D]; k, v, dk, dv: [B, n_k, H, D] device tensors of one
+    dtype (bfloat16 or float32), last dim contiguous; q-side tensors (q, dq
+    and the outputs o, d_o) share strides, as do the k-side ones.  Pass
+    dq = dk = dv = None for the primal only (then d_o is None).  Outputs are
+    allocated when not given.  The call is asynchronous on ``stream`` (default:
+    torch's current stream).  Returns (o, d_o, lse) with lse [B, H, n_q] fp32.
+    """
+    import torch
+    tangent = dq is not None or dk is not None or dv is not None
+    if tangent and (dq is None or dk is None or dv is None):
+        raise ValueError("pass all of dq, dk, dv or none of them")
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("tensors must be [B, N, H, D]")
+    B, n_q, H, D = q.shape
+    n_k = k.shape[1]
+    for name, t, rows in (("k", k, n_k), ("v", v, n_k), ("dq", dq, n_q), ("dk", dk, n_k),
+                          ("dv", dv, n_k)):
+        if t is None:
+            continue
+        if tuple(t.shape) != (B, rows, H, D):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {(B, rows, H, D)}")
+        if t.dtype != q.dtype or t.device != q.device:
+            raise ValueError(f"{name} differs from q in dtype or device")
+    if not q.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    code = _dtype_code(q)
+    if o is None:
+        o = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
+    if tangent and d_o is None:
+        d_o = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, n_q), dtype=torch.float32, device=q.device)
+    for name, t in (("dq", dq), ("o", o), ("d_o", d_o)):
+        if t is not None and (tuple(t.shape) != tuple(q.shape) or t.stride() != q.stride()
+                              or t.dtype != q.dtype):
+            raise ValueError(f"{name} must match q in shape, strides and dtype")
+    for name, t in (("v", v), ("dk", dk), ("dv", dv)):
+        if t is not None and t.stride() != k.stride():
+            raise ValueError(f"{name} must have the strides of k")
+    if q.stride(3) != 1 or k.stride(3) != 1:
+        raise ValueError("the last dimension must be contiguous")
+    if tuple(lse.shape) != (B, H, n_q) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, n_q] tensor")
+    ptr = lambda t: t.data_ptr() if t is not None else None
+    a = _lib.AttnJvpArgs(
+        dtype=code, B=B, H=H, n_q=n_q, n_k=n_k, D=D,
+        q=ptr(q), k=ptr(k), v=ptr(v), dq=ptr(dq), dk=ptr(dk), dv=ptr(dv),
+        o=ptr(o), d_o=ptr(d_o) if tangent else None, lse=ptr(lse),
+        q_stride_b=q.stride(0), q_stride_n=q.stride(1), q_stride_h=q.stride(2),
+        k_stride_b=k.stride(0), k_stride_n=k.stride(1), k_stride_h=k.stride(2),
+        scale=float(scale) if scale is not None else 0.0)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    with torch.cuda.device(q.device):
+        st = _lib.lib().attn_jvp_fwd(ctypes.byref(a), mask.handle, ctypes.c_void_p(handle))
+    _check(st, "attn_jvp_fwd")
+    return o, (d_o if tangent else None), lse

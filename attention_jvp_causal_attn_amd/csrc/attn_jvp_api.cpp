@@ -1,0 +1,181 @@
+// C ABI entry points: argument validation, per-device schedule upload and
+// kernel dispatch.  Every tensor stays caller-owned device memory; the only
+// device memory the library owns is the per-mask tile schedule.
+#include <cmath>
+#include <cstring>
+
+#include "internal.h"
+
+using attnjvp::DeviceSchedule;
+using attnjvp::HostSchedule;
+using attnjvp::KernelParams;
+
+namespace {
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Upload (once per device and tile shape) the schedule of m; caller holds m->mu.
+int device_schedule_locked(const attn_jvp_mask *m, int device, int BM, int BN,
+                           const DeviceSchedule **out) {
+  auto key = std::make_tuple(device, BM, BN);
+  auto it = m->dev_sched.find(key);
+  if (it != m->dev_sched.end()) {
+    *out = &it->second;
+    return ATTN_JVP_OK;
+  }
+  int st = ATTN_JVP_OK;
+  const HostSchedule *hs = attnjvp::host_schedule_locked(m, BM, BN, &st);
+  if (!hs) return st;
+  const size_t n_entries = hs->entry_block.size();
+  const size_t off_bytes = (hs->tile_offsets.size() * 4 + 15) & ~size_t(15);
+  const size_t ord_bytes = (hs->tile_order.size() * 4 + 15) & ~size_t(15);
+  const size_t ent_bytes = (n_entries * 8 + 15) & ~size_t(15);
+  const size_t bit_bytes = hs->partial_bits.size() * 4;
+  const size_t total = off_bytes + ord_bytes + ent_bytes + bit_bytes + 16;
+  std::vector<uint8_t> blob;
+  try {
+    blob.assign(total, 0);
+  } catch (const std::bad_alloc &) {
+    return ATTN_JVP_ERR_OOM;
+  }
+  std::memcpy(blob.data(), hs->tile_offsets.data(), hs->tile_offsets.size() * 4);
+  std::memcpy(blob.data() + off_bytes, hs->tile_order.data(), hs->tile_order.size() * 4);
+  int32_t *ent = reinterpret_cast<int32_t *>(blob.data() + off_bytes + ord_bytes);
+  for (size_t e = 0; e < n_entries; ++e) {
+    ent[2 * e] = hs->entry_block[e];
+    ent[2 * e + 1] = hs->entry_partial[e];
+  }
+  if (bit_bytes)
+    std::memcpy(blob.data() + off_bytes + ord_bytes + ent_bytes, hs->partial_bits.data(), bit_bytes);
+  void *dptr = nullptr;
+  hipError_t err = hipMalloc(&dptr, total);
+  if (err == hipErrorOutOfMemory) return ATTN_JVP_ERR_OOM;
+  if (err != hipSuccess) return ATTN_JVP_ERR_HIP;
+  err = hipMemcpy(dptr, blob.data(), total, hipMemcpyHostToDevice);
+  if (err != hipSuccess) {
+    (void)hipFree(dptr);
+    return ATTN_JVP_ERR_HIP;
+  }
+  DeviceSchedule ds;
+  uint8_t *b = static_cast<uint8_t *>(dptr);
+  ds.base = dptr;
+  ds.tile_offsets = reinterpret_cast<const int32_t *>(b);
+  ds.tile_order = reinterpret_cast<const int32_t *>(b + off_bytes);
+  ds.entries = reinterpret_cast<const int2 *>(b + off_bytes + ord_bytes);
+  ds.partial_bits = reinterpret_cast<const uint32_t *>(b + off_bytes + ord_bytes + ent_bytes);
+  ds.n_tiles = hs->n_tiles;
+  auto res = m->dev_sched.emplace(key, ds);
+  *out = &res.first->second;
+  return ATTN_JVP_OK;
+}
+
+}  // namespace
+
+extern "C" void attn_jvp_mask_free(attn_jvp_mask *m) {
+  if (!m) return;
+  int cur = -1;
+  bool have_cur = hipGetDevice(&cur) == hipSuccess;
+  for (auto &kv : m->dev_sched) {
+    const int dev = std::get<0>(kv.first);
+    if (hipSetDevice(dev) == hipSuccess) (void)hipFree(kv.second.base);
+  }
+  if (have_cur && !m->dev_sched.empty()) (void)hipSetDevice(cur);
+  delete m;
+}
+
+extern "C" int attn_jvp_tile_shape(int32_t dtype, int32_t D, int32_t *block_m, int32_t *block_n) {
+  if (!block_m || !block_n) return ATTN_JVP_ERR_NULL;
+  if (dtype != ATTN_JVP_BF16 && dtype != ATTN_JVP_F32) return ATTN_JVP_ERR_DTYPE;
+  if (D != 64 && D != 128) return ATTN_JVP_ERR_UNSUPPORTED;
+  if (dtype == ATTN_JVP_BF16) {
+    *block_m = attnjvp::kBf16BlockM;
+    *block_n = attnjvp::kBf16BlockN;
+  } else {
+    *block_m = attnjvp::kF32BlockM;
+    *block_n = attnjvp::kF32BlockN;
+  }
+  return ATTN_JVP_OK;
+}
+
+extern "C" int attn_jvp_fwd(const attn_jvp_args *a, const attn_jvp_mask *m, void *stream) {
+  if (!a || !m) return ATTN_JVP_ERR_NULL;
+  if (a->dtype != ATTN_JVP_BF16 && a->dtype != ATTN_JVP_F32) return ATTN_JVP_ERR_DTYPE;
+  if (!a->q || !a->k || !a->v || !a->o || !a->lse) return ATTN_JVP_ERR_NULL;
+  const int n_tan = (a->dq != nullptr) + (a->dk != nullptr) + (a->dv != nullptr);
+  if (n_tan != 0 && n_tan != 3) return ATTN_JVP_ERR_UNSUPPORTED;
+  const bool tangent = n_tan == 3;
+  if (tangent && !a->d_o) return ATTN_JVP_ERR_NULL;
+  if (a->B <= 0 || a->H <= 0 || a->n_q <= 0 || a->n_k <= 0) return ATTN_JVP_ERR_SHAPE;
+  if (a->D != 64 && a->D != 128) return ATTN_JVP_ERR_UNSUPPORTED;
+  if (a->n_q != m->n_q || a->n_k != m->n_k) return ATTN_JVP_ERR_MASK;
+  if (!(std::isfinite(a->scale))) return ATTN_JVP_ERR_SHAPE;
+  if (int64_t(a->B) * a->H * a->n_q > (int64_t(1) << 40)) return ATTN_JVP_ERR_SHAPE;
+  const int64_t es = a->dtype == ATTN_JVP_BF16 ? 2 : 4;
+  const int64_t qs[3] = {a->q_stride_b, a->q_stride_n, a->q_stride_h};
+  const int64_t ks[3] = {a->k_stride_b, a->k_stride_n, a->k_stride_h};
+  for (int i = 0; i < 3; ++i) {
+    if (qs[i] < 0 || ks[i] < 0) return ATTN_JVP_ERR_SHAPE;
+    if ((qs[i] * es) % 16 || (ks[i] * es) % 16) return ATTN_JVP_ERR_ALIGN;
+  }
+  // rows of one head must not overlap the D contiguous elements of another
+  if (a->H > 1 && (qs[2] < a->D || ks[2] < a->D)) return ATTN_JVP_ERR_SHAPE;
+  const void *ins[6] = {a->q, a->k, a->v, a->dq, a->dk, a->dv};
+  const void *outs[2] = {a->o, a->d_o};
+  for (const void *p : ins)
+    if (p && !aligned16(p)) return ATTN_JVP_ERR_ALIGN;
+  for (const void *p : outs)
+    if (p && !aligned16(p)) return ATTN_JVP_ERR_ALIGN;
+  if (!aligned16(a->lse)) return ATTN_JVP_ERR_ALIGN;
+  for (const void *p : ins)
+    for (const void *o : outs)
+      if (p && o && p == o) return ATTN_JVP_ERR_UNSUPPORTED;
+  if (tangent && a->o == a->d_o) return ATTN_JVP_ERR_UNSUPPORTED;
+
+  int device = -1;
+  if (hipGetDevice(&device) != hipSuccess) return ATTN_JVP_ERR_HIP;
+  int BM = 0, BN = 0;
+  attn_jvp_tile_shape(a->dtype, a->D, &BM, &BN);
+  const DeviceSchedule *ds = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(m->mu);
+    int st = device_schedule_locked(m, device, BM, BN, &ds);
+    if (st != ATTN_JVP_OK) return st;
+  }
+  if (int64_t(ds->n_tiles) * a->B * a->H > int64_t(0x7fffffff)) return ATTN_JVP_ERR_SHAPE;
+
+  KernelParams p;
+  p.q = a->q; p.k = a->k; p.v = a->v;
+  p.dq = a->dq; p.dk = a->dk; p.dv = a->dv;
+  p.o = a->o; p.d_o = tangent ? a->d_o : nullptr;
+  p.lse = a->lse;
+  p.q_sb = a->q_stride_b; p.q_sn = a->q_stride_n; p.q_sh = a->q_stride_h;
+  p.k_sb = a->k_stride_b; p.k_sn = a->k_stride_n; p.k_sh = a->k_stride_h;
+  p.B = a->B; p.H = a->H; p.n_q = a->n_q; p.n_k = a->n_k;
+  p.scale = a->scale > 0.f ? a->scale : 1.0f / std::sqrt(float(a->D));
+  p.scale_log2 = float(double(p.scale) * 1.4426950408889634);
+  p.tile_offsets = ds->tile_offsets;
+  p.tile_order = ds->tile_order;
+  p.entries = ds->entries;
+  p.partial_bits = ds->partial_bits;
+  p.n_tiles = ds->n_tiles;
+  int err = a->dtype == ATTN_JVP_BF16 ? attnjvp::launch_bf16(p, a->D, tangent, stream)
+                                       : attnjvp::launch_f32(p, a->D, tangent, stream);
+  return err == hipSuccess ? ATTN_JVP_OK : ATTN_JVP_ERR_HIP;
+}
+
+extern "C" const char *attn_jvp_status_str(int status) {
+  switch (status) {
+    case ATTN_JVP_OK: return "ok";
+    case ATTN_JVP_ERR_NULL: return "required pointer is NULL";
+    case ATTN_JVP_ERR_SHAPE: return "invalid or inconsistent sizes";
+    case ATTN_JVP_ERR_DTYPE: return "unknown dtype";
+    case ATTN_JVP_ERR_ALIGN: return "pointer or stride not 16-byte aligned";
+    case ATTN_JVP_ERR_MASK: return "malformed mask or mask size mismatch";
+    case ATTN_JVP_ERR_UNSUPPORTED: return "unsupported configuration";
+    case ATTN_JVP_ERR_HIP: return "HIP device unavailable or HIP call failed";
+    case ATTN_JVP_ERR_OOM: return "out of memory";
+    default: return "unknown status";
+  }
+}
+
+extern "C" int attn_jvp_version(void) { return ATTN_JVP_API_VERSION; }

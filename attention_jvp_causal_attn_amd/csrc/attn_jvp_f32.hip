@@ -1,0 +1,182 @@
+// Fused primal + tangent masked attention in fp32 (fp32 in, fp32 arithmetic).
+//
+// The same online-softmax recurrence as the bf16 kernel ("Causal-rCM ..."
+// summary, Appendix B: tangent and primal share one pass and one rescaling;
+// masked pairs carry no tangent) done on the vector ALUs in full fp32, so the
+// result stays within fp32 rounding of the exact operator (no reduced-
+// precision products anywhere).  This path serves small fp32 problems; it is
+// not the throughput path.
+//
+// Layout: a workgroup of 256 threads owns 64 query rows of one (batch, head);
+// 4 consecutive lanes share a row, each holding D/4 of its dimensions of q,
+// dq and the two accumulators.  Key blocks of 32 rows of K, dK, V, dV are
+// staged in LDS; per key the 4 lanes reduce their partial dot products with
+// two xor-shuffles (every lane ends with the same bits).
+#include <hip/hip_runtime.h>
+
+#include "internal.h"
+
+namespace attnjvp {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int BM = kF32BlockM;  // 64 rows
+constexpr int BN = kF32BlockN;  // 32 keys
+constexpr int TPR = 4;          // lanes per row
+static_assert(BM * TPR == kThreads, "one row per 4 lanes");
+constexpr float kNegInf = -__builtin_inff();
+
+__device__ __forceinline__ int xcd_logical(int w, int G) {
+  const int xcd = w & 7, local = w >> 3;
+  const int q = G >> 3, r = G & 7;
+  return xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
+}
+
+template <int D, bool TAN>
+__global__ __launch_bounds__(kThreads) void attn_jvp_f32_kernel(KernelParams p) {
+  constexpr int DS = D / TPR;   // dims per lane
+  constexpr int LD = D + 4;     // padded LDS row (floats)
+  __shared__ float Ks[BN * LD], dKs[BN * LD], Vs[BN * LD], dVs[BN * LD];
+
+  const int G = p.n_tiles * p.B * p.H;
+  const int L = xcd_logical(int(blockIdx.x), G);
+  const int slot = L % p.n_tiles;
+  const int bh = L / p.n_tiles;
+  const int head = bh % p.H, batch = bh / p.H;
+  const int tile = p.tile_order[slot];
+
+  const int tid = threadIdx.x;
+  const int row_in_tile = tid / TPR, part = tid % TPR;
+  const int qrow = tile * BM + row_in_tile;
+  const bool qvalid = qrow < p.n_q;
+  const int d0 = part * DS;
+
+  const int64_t qoff = int64_t(batch) * p.q_sb + int64_t(head) * p.q_sh + int64_t(qrow) * p.q_sn;
+  const int64_t koff = int64_t(batch) * p.k_sb + int64_t(head) * p.k_sh;
+  const float *kg = static_cast<const float *>(p.k) + koff;
+  const float *vg = static_cast<const float *>(p.v) + koff;
+  const float *dkg = TAN ? static_cast<const float *>(p.dk) + koff : nullptr;
+  const float *dvg = TAN ? static_cast<const float *>(p.dv) + koff : nullptr;
+
+  float q[DS], dq[DS], acc[DS], tac[DS];
+#pragma unroll
+  for (int e = 0; e < DS; ++e) {
+    q[e] = qvalid ? static_cast<const float *>(p.q)[qoff + d0 + e] : 0.f;
+    dq[e] = (TAN && qvalid) ? static_cast<const float *>(p.dq)[qoff + d0 + e] : 0.f;
+    acc[e] = 0.f;
+    tac[e] = 0.f;
+  }
+  float m_run = kNegInf, l_run = 0.f, mu_run = 0.f;
+
+  const int e0 = p.tile_offsets[tile], e1 = p.tile_offsets[tile + 1];
+  for (int e = e0; e < e1; ++e) {
+    const int2 ent = p.entries[e];
+    const int key0 = ent.x * BN;
+    __syncthreads();
+    for (int i = tid; i < BN * D / 4; i += kThreads) {
+      const int r = i / (D / 4), c = (i % (D / 4)) * 4;
+      const int key = key0 + r;
+      float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+      float4 kk = z, vv = z, dkk = z, dvv = z;
+      if (key < p.n_k) {
+        const int64_t off = int64_t(key) * p.k_sn + c;
+        kk = *reinterpret_cast<const float4 *>(kg + off);
+        vv = *reinterpret_cast<const float4 *>(vg + off);
+        if (TAN) {
+          dkk = *reinterpret_cast<const float4 *>(dkg + off);
+          dvv = *reinterpret_cast<const float4 *>(dvg + off);
+        }
+      }
+      *reinterpret_cast<float4 *>(&Ks[r * LD + c]) = kk;
+      *reinterpret_cast<float4 *>(&Vs[r * LD + c]) = vv;
+      if (TAN) {
+        *reinterpret_cast<float4 *>(&dKs[r * LD + c]) = dkk;
+        *reinterpret_cast<float4 *>(&dVs[r * LD + c]) = dvv;
+      }
+    }
+    __syncthreads();
+    const uint32_t bits = ent.y >= 0 ? p.partial_bits[int64_t(ent.y) * BM + row_in_tile] : ~0u;
+
+    float s[BN], ds[BN];
+    float mx = kNegInf;
+#pragma unroll
+    for (int j = 0; j < BN; ++j) {
+      float a = 0.f, b = 0.f;
+#pragma unroll
+      for (int x = 0; x < DS; ++x) {
+        a = fmaf(q[x], Ks[j * LD + d0 + x], a);
+        if (TAN) {
+          b = fmaf(dq[x], Ks[j * LD + d0 + x], b);
+          b = fmaf(q[x], dKs[j * LD + d0 + x], b);
+        }
+      }
+      a += __shfl_xor(a, 1, 64);
+      a += __shfl_xor(a, 2, 64);
+      if (TAN) {
+        b += __shfl_xor(b, 1, 64);
+        b += __shfl_xor(b, 2, 64);
+      }
+      const bool ok = (bits >> j) & 1u;
+      s[j] = ok ? a * p.scale : kNegInf;
+      ds[j] = ok ? b * p.scale : 0.f;
+      mx = fmaxf(mx, s[j]);
+    }
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = m_new == kNegInf ? 0.f : m_new;
+    const float alpha = expf(m_run - m_use);
+    float lsum = 0.f, musum = 0.f;
+#pragma unroll
+    for (int j = 0; j < BN; ++j) {
+      s[j] = expf(s[j] - m_use);  // now the weight p_j
+      lsum += s[j];
+      if (TAN) musum += s[j] * ds[j];
+    }
+    l_run = l_run * alpha + lsum;
+    if (TAN) mu_run = mu_run * alpha + musum;
+    m_run = m_new;
+#pragma unroll
+    for (int x = 0; x < DS; ++x) {
+      float a = acc[x] * alpha, t = tac[x] * alpha;
+#pragma unroll
+      for (int j = 0; j < BN; ++j) {
+        const float vj = Vs[j * LD + d0 + x];
+        a = fmaf(s[j], vj, a);
+        if (TAN) t = fmaf(s[j], fmaf(ds[j], vj, dVs[j * LD + d0 + x]), t);
+      }
+      acc[x] = a;
+      tac[x] = t;
+    }
+  }
+
+  if (!qvalid) return;
+  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+  const float mu_n = mu_run * inv;
+  if (part == 0)
+    p.lse[(int64_t(batch) * p.H + head) * p.n_q + qrow] = l_run > 0.f ? m_run + logf(l_run) : kNegInf;
+  float *o = static_cast<float *>(p.o) + qoff + d0;
+  float *dout = TAN ? static_cast<float *>(p.d_o) + qoff + d0 : nullptr;
+#pragma unroll
+  for (int x = 0; x < DS; ++x) {
+    const float ov = acc[x] * inv;
+    o[x] = ov;
+    if (TAN) dout[x] = tac[x] * inv - ov * mu_n;
+  }
+}
+
+template <int D, bool TAN>
+hipError_t launch(const KernelParams &p, hipStream_t stream) {
+  const int64_t G = int64_t(p.n_tiles) * p.B * p.H;
+  hipLaunchKernelGGL((attn_jvp_f32_kernel<D, TAN>), dim3(unsigned(G)), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int launch_f32(const KernelParams &p, int D, bool tangent, void *stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (D == 128) return tangent ? launch<128, true>(p, s) : launch<128, false>(p, s);
+  if (D == 64) return tangent ? launch<64, true>(p, s) : launch<64, false>(p, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace attnjvp

@@ -1,0 +1,89 @@
+// Internal declarations shared by the host library and the gfx950 kernels.
+#pragma once
+
+#include <cstdint>
+#include <map>
+#include <mutex>
+#include <tuple>
+#include <vector>
+
+#include <hip/hip_runtime.h>
+
+#include "attn_jvp.h"
+
+namespace attnjvp {
+
+// Host-side block schedule of one mask for one tile shape (see
+// attn_jvp_mask_schedule in attn_jvp.h for the meaning of every array).
+struct HostSchedule {
+  int32_t block_m = 0, block_n = 0;
+  int32_t n_tiles = 0;
+  std::vector<int32_t> tile_offsets;   // n_tiles + 1
+  std::vector<int32_t> tile_order;     // n_tiles, heaviest first
+  std::vector<int32_t> entry_block;    // n_entries
+  std::vector<int32_t> entry_partial;  // n_entries, -1 = full block
+  std::vector<uint32_t> partial_bits;  // n_partial * block_m * (block_n / 32)
+  int64_t n_partial = 0;
+};
+
+// One device copy of a schedule: a single allocation holding, in order,
+// tile_offsets, tile_order, entries (block, partial) interleaved, bits.
+struct DeviceSchedule {
+  void *base = nullptr;
+  const int32_t *tile_offsets = nullptr;
+  const int32_t *tile_order = nullptr;
+  const int2 *entries = nullptr;
+  const uint32_t *partial_bits = nullptr;
+  int32_t n_tiles = 0;
+};
+
+// Everything a kernel launch needs, passed by value.
+struct KernelParams {
+  const void *q, *k, *v, *dq, *dk, *dv;
+  void *o, *d_o;
+  float *lse;
+  int64_t q_sb, q_sn, q_sh;
+  int64_t k_sb, k_sn, k_sh;
+  int32_t B, H, n_q, n_k;
+  float scale;        // softmax scale
+  float scale_log2;   // scale * log2(e): scores go to exp2 directly
+  const int32_t *tile_offsets;
+  const int32_t *tile_order;
+  const int2 *entries;
+  const uint32_t *partial_bits;
+  int32_t n_tiles;
+};
+
+}  // namespace attnjvp
+
+struct attn_jvp_mask {
+  int32_t n_q = 0, n_k = 0;
+  std::vector<int32_t> group_q_begin;  // n_groups + 1
+  std::vector<int32_t> range_ptr;      // n_groups + 1
+  std::vector<int32_t> k_begin, k_end; // n_ranges
+  int64_t n_visible = 0;
+
+  mutable std::mutex mu;
+  // (block_m, block_n) -> host schedule
+  mutable std::map<std::pair<int, int>, attnjvp::HostSchedule> host_sched;
+  // (device, block_m, block_n) -> device copy
+  mutable std::map<std::tuple<int, int, int>, attnjvp::DeviceSchedule> dev_sched;
+};
+
+namespace attnjvp {
+
+// Build (or fetch the cached) host schedule; caller holds m->mu.
+const HostSchedule *host_schedule_locked(const attn_jvp_mask *m, int block_m,
+                                         int block_n, int *status);
+
+// Kernel launchers (defined in the .hip files).  Return a hipError_t value.
+int launch_bf16(const KernelParams &p, int D, bool tangent, void *stream);
+int launch_f32(const KernelParams &p, int D, bool tangent, void *stream);
+
+// Tile shapes of the kernels.
+constexpr int kBf16BlockM = 128;
+constexpr int kBf16BlockN = 32;
+constexpr int kF32BlockM = 64;
+constexpr int kF32BlockN = 32;
+
+}  // namespace attnjvp

@@ -1,0 +1,213 @@
+"""Throughput of the fused attention JVP (primal + tangent) on one MI355X.
+
+One step = one ``attn_jvp_fwd`` call over the whole workload (every query tile
+of every (batch, head)), inputs resident in HBM.  Default workload: the
+chunk-wise teacher-forcing mask at causal Wan2.1-1.3B attention shapes
+(B=1, H=12, D=128, 21 clean + 21 noisy latent frames of 1560 tokens in chunks
+of 3 frames, N = 65,520), bf16.
+
+Prints one JSON line on stdout; progress goes to stderr.
+
+  python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload 3]
+                  [--no-cpu-baseline] [--copy-calibration]
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_F32_VALU_TFLOPS = 157.3
+KERNEL_SOURCES = ["attention_jvp_causal_attn_amd/csrc/attn_jvp_bf16.hip"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_jvp_bf16_chunkwise65k_traffic.md")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def visible_pairs(w):
+    """Admissible pairs per (b, h) under the TF mask: 2F groups of C rows, the
+    groups of unit u seeing (u + 1) C keys: C^2 F (F + 1)."""
+    F, C = w.n_units, w.unit_tokens
+    return C * C * F * (F + 1)
+
+
+def kernel_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload_name):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, when it
+    was taken on the current kernel source and this workload; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    src = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    wl = re.search(r"workload:\s*(\S+)", text)
+    tb = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not (src and wl and tb) or src.group(1) != kernel_hash() or wl.group(1) != workload_name:
+        return None
+    return float(tb.group(1))
+
+
+def time_calls(fn, steps, warmup, stream):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
+    for i in range(steps):
+        fn()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    total = ev[0].elapsed_time(ev[-1])
+    return total / steps, per
+
+
+def cpu_baseline(w, x, target_s=15.0):
+    """The fp64 oracle on a bounded sample of the same workload: query rows of
+    slice (b=0, h=0) spread over every unit of both streams, sized to about
+    ``target_s`` seconds of host time; scaled to TFLOP/s with the same
+    12*D-per-admissible-pair count as the GPU figure."""
+    import numpy as np
+    from oracle import masked_attention_jvp, tf_allowed
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([t.get("num_threads", 1) for t in threadpool_info()
+                       if t.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    pred = tf_allowed(w.n_frames, w.tokens_per_frame, w.frames_per_chunk)
+    sl = {k: v[:1, :, :1] for k, v in x.items()}          # slice (b=0, h=0)
+    rng = np.random.default_rng(12345)
+
+    def run(n_rows):
+        rows = np.sort(rng.choice(w.N, size=n_rows, replace=False))
+        pairs = int(pred(rows).sum())
+        t0 = time.perf_counter()
+        masked_attention_jvp(sl["q"], sl["k"], sl["v"], sl["dq"], sl["dk"], sl["dv"], pred,
+                             rows=rows)
+        return time.perf_counter() - t0, pairs, n_rows
+
+    dt, pairs, n = run(64)
+    if dt < target_s / 3:
+        n2 = int(min(w.N, max(64, 64 * target_s / max(dt, 1e-3))))
+        dt, pairs, n = run(n2)
+    tflops = 12 * w.D * pairs / dt / 1e12
+    return {"value": tflops, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"fp64 numpy oracle on {n} random query rows of one (b,h) slice "
+                       f"({pairs} admissible pairs, {dt:.1f} s), scaled by 12*D FLOP per pair")}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-primal", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (for HBM counter scaling)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(every (batch, head) slice is independent; see the sharding notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import attention_jvp_causal_attn_amd as aj
+    from attention_jvp_causal_attn_amd.inputs import WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload]
+    log(f"workload: {w.describe()}")
+    t0 = time.perf_counter()
+    x = make_inputs(w)
+    xd = {k: v.to("cuda") for k, v in x.items()}
+    torch.cuda.synchronize()
+    log(f"inputs ready in {time.perf_counter() - t0:.1f} s")
+    mask = aj.attn_jvp_mask_tf(w.n_frames, w.tokens_per_frame, w.frames_per_chunk)
+    pairs = mask.info()["n_visible_pairs"]
+    assert pairs == visible_pairs(w)
+    flops = 12 * w.D * pairs * w.B * w.H
+    pflops = 4 * w.D * pairs * w.B * w.H
+    B, N, H, D = xd["q"].shape
+    o = torch.empty_like(xd["q"])
+    do = torch.empty_like(xd["q"])
+    lse = torch.empty(B, H, N, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def jvp():
+        aj.attn_jvp_fwd(xd["q"], xd["k"], xd["v"], xd["dq"], xd["dk"], xd["dv"], mask,
+                        o=o, d_o=do, lse=lse, stream=stream)
+
+    def primal():
+        aj.attn_jvp_fwd(xd["q"], xd["k"], xd["v"], None, None, None, mask, o=o, lse=lse,
+                        stream=stream)
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 29, dtype=torch.float16, device="cuda")   # 1 GiB
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log("copy calibration: 3 x 1 GiB device copies done")
+
+    ms, per = time_calls(jvp, args.steps, args.warmup, stream)
+    per_sorted = sorted(per)
+    value = flops / (ms * 1e-3) / 1e12
+    log(f"JVP: {ms:.3f} ms/call, {value:.1f} TFLOP/s "
+        f"({100 * value / PEAK_BF16_TFLOPS:.1f}% of bf16 peak)")
+    res = {
+        "metric": "attention-JVP TFLOP/s (primal+tangent) and % of bf16 MFMA peak, 1 GPU",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded Gaussian Q, K, V, tangents at Wan2.1-1.3B attention shapes)",
+        "config": {"workload": w.name, "mask": w.describe(), "B": w.B, "H": w.H, "D": w.D,
+                   "N": w.N, "visible_pairs_per_slice": pairs,
+                   "algorithmic_flop_per_call": flops, "parallelism": "single GPU"},
+        "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "ms_p10": round(per_sorted[len(per) // 10], 4),
+        "ms_median": round(per_sorted[len(per) // 2], 4),
+        "ms_p90": round(per_sorted[(9 * len(per)) // 10], 4),
+    }
+    if not args.no_primal:
+        pms, _ = time_calls(primal, args.steps, args.warmup, stream)
+        pval = pflops / (pms * 1e-3) / 1e12
+        log(f"primal only: {pms:.3f} ms/call, {pval:.1f} TFLOP/s; JVP/primal time {ms / pms:.2f}")
+        res["primal_only"] = {"ms_per_step": round(pms, 4), "tflops": round(pval, 2),
+                              "jvp_over_primal_time": round(ms / pms, 3)}
+    traffic = measured_traffic(w.name)
+    res["roofline"] = {"bound": "mfma", "achieved": round(value, 2), "peak": PEAK_BF16_TFLOPS,
+                       "unit": "TFLOP/s", "frac": round(value / PEAK_BF16_TFLOPS, 4),
+                       "traffic": traffic}
+    if not args.no_cpu_baseline:
+        log("timing the fp64 CPU oracle on a sample ...")
+        res["cpu_baseline"] = cpu_baseline(w, x)
+        log(f"cpu baseline: {res['cpu_baseline']}")
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,187 @@
+/*
+ * attn_jvp.h -- C ABI of the MI355X (gfx950) forward-mode JVP of masked
+ * scaled-dot-product attention.
+ *
+ * Operation ("Causal-rCM: A Unified Teacher-Forcing and Self-Forcing Open
+ * Recipe ..." summary, Appendix B "FlashAttention-2 JVP Kernel with Custom
+ * Masks"): given Q, K, V and their tangents dQ, dK, dV, compute in one
+ * online-softmax pass the primal masked attention output O, its row
+ * log-sum-exp LSE and the tangent dO, the directional derivative of exactly
+ * the same masked operator.  Masked-out pairs contribute no tangent (the mask
+ * is discrete).  For query row i with admissible keys J_i:
+ *
+ *   s_j = scale <q_i,k_j>,  p = softmax_{J_i}(s),  O_i = sum_j p_j v_j,
+ *   LSE_i = ln sum_{j in J_i} exp(s_j),
+ *   ds_j = scale (<dq_i,k_j> + <q_i,dk_j>),  mu_i = sum_j p_j ds_j,
+ *   dO_i = sum_j p_j (ds_j - mu_i) v_j + sum_j p_j dv_j.
+ *
+ * Masks are query groups with admissible key ranges (Appendix B: custom masks
+ * as query-key rectangles, one sparse schedule shared by the primal and the
+ * tangent scores).  The teacher-forcing builder packs [clean | noisy] tokens
+ * (Section 3 of the same page: the TF-masked packed forward; "Causal Forcing:
+ * Autoregressive Diffusion Distillation Done Right ..." summary, Section 2:
+ * clean and noisy videos concatenated under a causal attention mask).
+ *
+ * Conventions for every entry point:
+ *   - returns ATTN_JVP_OK (0) or a negative status; never throws, never
+ *     aborts, never writes through a pointer after returning an error;
+ *   - all int32/int64 sizes are element counts;
+ *   - host pointers are read during the call only; nothing is retained.
+ */
+#ifndef ATTN_JVP_H
+#define ATTN_JVP_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_JVP_API_VERSION 1
+
+enum attn_jvp_status {
+  ATTN_JVP_OK = 0,
+  ATTN_JVP_ERR_NULL = -1,        /* a required pointer is NULL */
+  ATTN_JVP_ERR_SHAPE = -2,       /* sizes inconsistent or out of range */
+  ATTN_JVP_ERR_DTYPE = -3,       /* unknown dtype code */
+  ATTN_JVP_ERR_ALIGN = -4,       /* pointer or stride not 16-byte aligned, or
+                                    last dimension not contiguous */
+  ATTN_JVP_ERR_MASK = -5,        /* malformed mask description, or mask size
+                                    differs from the tensors */
+  ATTN_JVP_ERR_UNSUPPORTED = -6, /* valid but not implemented (head dim,
+                                    partly-NULL tangents, aliasing outputs) */
+  ATTN_JVP_ERR_HIP = -7,         /* no usable HIP device, or a HIP call failed */
+  ATTN_JVP_ERR_OOM = -8          /* host or device allocation failed */
+};
+
+enum attn_jvp_dtype {
+  ATTN_JVP_BF16 = 0, /* inputs and O/dO in bfloat16; bf16 MFMA, fp32 accumulate */
+  ATTN_JVP_F32 = 1   /* inputs and O/dO in fp32; fp32 arithmetic throughout */
+};
+
+/* Opaque, immutable mask descriptor: a partition of the query rows [0, n_q)
+ * into contiguous groups, each with a sorted list of disjoint key intervals
+ * [k_begin, k_end) in [0, n_k).  Library-owned host memory plus lazily built
+ * per-device tile schedules.  Safe to share between threads once built. */
+typedef struct attn_jvp_mask attn_jvp_mask;
+
+/* Teacher-forcing mask over the packed sequence [clean | noisy], each stream
+ * n_frames * tokens_per_frame tokens (N = 2 * n_frames * tokens_per_frame).
+ * A unit is frames_per_chunk consecutive frames (1 = frame-wise).  A clean
+ * token of unit u sees clean units <= u; a noisy token of unit u sees clean
+ * units < u and the noisy tokens of unit u (all of them, in both directions).
+ * Errors: ERR_NULL (out == NULL); ERR_SHAPE (a size <= 0, n_frames not a
+ * multiple of frames_per_chunk, or N > 2^30); ERR_OOM.  On success *out owns a
+ * new mask; release it with attn_jvp_mask_free. */
+int attn_jvp_mask_tf(int32_t n_frames, int32_t tokens_per_frame,
+                     int32_t frames_per_chunk, attn_jvp_mask **out);
+
+/* Generic query-key rectangles in CSR form.
+ *   group_q_begin[n_groups + 1]: strictly increasing, group_q_begin[0] = 0,
+ *                                group_q_begin[n_groups] = n_q;
+ *   range_ptr[n_groups + 1]:     non-decreasing, range_ptr[0] = 0; group g owns
+ *                                ranges range_ptr[g] .. range_ptr[g+1]-1;
+ *   k_begin[r], k_end[r]:        0 <= k_begin <= k_end <= n_k; within a group
+ *                                sorted by k_begin and non-overlapping
+ *                                (touching ranges are merged, empty ones
+ *                                dropped).
+ * Errors: ERR_NULL; ERR_SHAPE (n_q, n_k <= 0 or > 2^30, n_groups <= 0);
+ * ERR_MASK (any rule above broken); ERR_OOM.  The stored form is canonical:
+ * adjacent groups with identical key sets are merged. */
+int attn_jvp_mask_rects(int32_t n_q, int32_t n_k, int32_t n_groups,
+                        const int32_t *group_q_begin, const int32_t *range_ptr,
+                        const int32_t *k_begin, const int32_t *k_end,
+                        attn_jvp_mask **out);
+
+/* Every query sees every key (plain attention): one group, one range. */
+int attn_jvp_mask_dense(int32_t n_q, int32_t n_k, attn_jvp_mask **out);
+
+/* Sizes of a mask; any output pointer may be NULL.  n_visible_pairs is the
+ * number of admissible (query, key) pairs. Errors: ERR_NULL (m == NULL). */
+int attn_jvp_mask_info(const attn_jvp_mask *m, int32_t *n_q, int32_t *n_k,
+                       int32_t *n_groups, int32_t *n_ranges,
+                       int64_t *n_visible_pairs);
+
+/* Copy the canonical CSR form out (arrays sized from attn_jvp_mask_info:
+ * n_groups + 1, n_groups + 1, n_ranges, n_ranges).  Errors: ERR_NULL. */
+int attn_jvp_mask_export(const attn_jvp_mask *m, int32_t *group_q_begin,
+                         int32_t *range_ptr, int32_t *k_begin, int32_t *k_end);
+
+/* Host copy of the block schedule the kernels use for a tile shape
+ * (block_m query rows x block_n keys, block_n a multiple of 32).  For query
+ * tile t (rows [t*block_m, (t+1)*block_m)), entries tile_offsets[t] ..
+ * tile_offsets[t+1]-1 list, in increasing order, the key blocks b (keys
+ * [b*block_n, (b+1)*block_n)) holding at least one admissible pair of the
+ * tile.  entry_partial[e] is -1 when every (row, key) of the block is
+ * admissible for every row of the tile that exists, else an index p into
+ * partial_bits, where word
+ *   partial_bits[(p * block_m + r) * (block_n / 32) + w]
+ * bit i says whether row t*block_m + r may see key b*block_n + 32*w + i.
+ * tile_order[n_tiles] lists the tiles by decreasing entry count (ties by
+ * index): the kernels launch heavy tiles first.
+ * Call with all array pointers NULL to get n_tiles / n_entries / n_partial,
+ * then again with arrays of those sizes.  Errors: ERR_NULL (m or a size
+ * pointer), ERR_SHAPE (block_m <= 0, block_n <= 0 or not a multiple of 32),
+ * ERR_OOM. */
+int attn_jvp_mask_schedule(const attn_jvp_mask *m, int32_t block_m,
+                           int32_t block_n, int32_t *n_tiles,
+                           int64_t *n_entries, int64_t *n_partial,
+                           int32_t *tile_offsets, int32_t *tile_order,
+                           int32_t *entry_block, int32_t *entry_partial,
+                           uint32_t *partial_bits);
+
+/* Release a mask and its device schedules.  The caller must make sure no
+ * launched work still uses it (synchronise the streams first).  NULL is a
+ * no-op. */
+void attn_jvp_mask_free(attn_jvp_mask *m);
+
+/* Arguments of one forward call.  Tensors are caller-owned device memory in
+ * [B, N, H, D] order with element strides (the last dimension contiguous):
+ * Q, dQ, O, dO use the q_stride_* strides and n_q rows; K, V, dK, dV use the
+ * k_stride_* strides and n_k rows.  LSE is [B, H, n_q] fp32, contiguous,
+ * natural log.  Every tensor pointer and every stride in bytes must be a
+ * multiple of 16. */
+typedef struct attn_jvp_args {
+  int32_t dtype;       /* enum attn_jvp_dtype */
+  int32_t B, H;        /* batch, heads (> 0) */
+  int32_t n_q, n_k;    /* query rows, key rows: must equal the mask's */
+  int32_t D;           /* head dim: 64 or 128 */
+  const void *q, *k, *v;
+  const void *dq, *dk, *dv; /* all non-NULL: JVP; all NULL: primal only (d_o
+                               untouched); mixed: ERR_UNSUPPORTED */
+  void *o, *d_o;            /* outputs; must not alias any input */
+  float *lse;               /* output, required */
+  int64_t q_stride_b, q_stride_n, q_stride_h;
+  int64_t k_stride_b, k_stride_n, k_stride_h;
+  float scale;              /* softmax scale; <= 0 selects 1/sqrt(D) */
+} attn_jvp_args;
+
+/* Launch the fused primal + tangent pass on hip_stream (a hipStream_t; NULL
+ * means the default stream) of the current device.  Asynchronous: argument
+ * errors are returned before anything is launched; a failed launch returns
+ * ERR_HIP; faults inside the kernel surface at the caller's next
+ * synchronisation.  The first call for a (mask, device, tile shape) builds and
+ * uploads the tile schedule (a blocking device allocation and copy); later
+ * calls launch only.  Deterministic: no atomics, fixed reduction order.
+ * Errors: ERR_NULL, ERR_DTYPE, ERR_SHAPE, ERR_ALIGN, ERR_MASK (mask sizes
+ * differ from n_q/n_k), ERR_UNSUPPORTED, ERR_HIP, ERR_OOM. */
+int attn_jvp_fwd(const attn_jvp_args *a, const attn_jvp_mask *m,
+                 void *hip_stream);
+
+/* Tile shape (query rows, keys) the kernel for (dtype, D) uses; these are the
+ * block_m / block_n of its schedule.  Errors: ERR_NULL, ERR_DTYPE,
+ * ERR_UNSUPPORTED (D not 64 or 128). */
+int attn_jvp_tile_shape(int32_t dtype, int32_t D, int32_t *block_m,
+                        int32_t *block_n);
+
+/* Static English text for a status code (never NULL). */
+const char *attn_jvp_status_str(int status);
+
+/* ATTN_JVP_API_VERSION of the built library. */
+int attn_jvp_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_JVP_H */

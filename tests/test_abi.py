@@ -1,0 +1,126 @@
+"""The C ABI library loads without a GPU, exports every declared entry point
+and rejects bad arguments with the documented status codes before touching
+the device."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import attention_jvp_causal_attn_amd as aj
+from attention_jvp_causal_attn_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn_jvp.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_jvp_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert "attn_jvp_fwd" in names and "attn_jvp_mask_tf" in names
+    handle = ctypes.CDLL(_lib.LIB_PATH)
+    for n in names:
+        assert hasattr(handle, n), n
+    assert set(names) == set(_lib.SIGNATURES)
+
+
+def test_version_and_status_strings():
+    assert aj.attn_jvp_version() == 1
+    for st in range(-8, 1):
+        assert aj.attn_jvp_status_str(st) not in ("", "unknown status")
+    assert aj.attn_jvp_status_str(-99) == "unknown status"
+    assert aj.attn_jvp_tile_shape(aj.ATTN_JVP_BF16, 128) == (128, 32)
+    assert aj.attn_jvp_tile_shape(aj.ATTN_JVP_F32, 64) == (64, 32)
+    with pytest.raises(aj.AttnJvpError):
+        aj.attn_jvp_tile_shape(aj.ATTN_JVP_BF16, 96)
+    with pytest.raises(aj.AttnJvpError):
+        aj.attn_jvp_tile_shape(7, 128)
+
+
+def _gpu_present():
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except Exception:
+        return False
+
+
+def _args(mask, **kw):
+    info = mask.info()
+    base = dict(dtype=0, B=1, H=2, n_q=info["n_q"], n_k=info["n_k"], D=128,
+                q=0x10000, k=0x20000, v=0x30000, dq=0x40000, dk=0x50000, dv=0x60000,
+                o=0x70000, d_o=0x80000, lse=0x90000,
+                q_stride_b=0, q_stride_n=256, q_stride_h=128,
+                k_stride_b=0, k_stride_n=256, k_stride_h=128, scale=0.0)
+    base.update(kw)
+    return _lib.AttnJvpArgs(**base)
+
+
+def _fwd(a, mask):
+    return _lib.lib().attn_jvp_fwd(ctypes.byref(a), mask.handle, None)
+
+
+# Every case fails validation before any HIP call, so fake (never dereferenced)
+# device addresses are safe here with or without a GPU.
+BAD = [
+    (dict(dtype=5), _lib.ATTN_JVP_ERR_DTYPE),
+    (dict(q=None), _lib.ATTN_JVP_ERR_NULL),
+    (dict(o=None), _lib.ATTN_JVP_ERR_NULL),
+    (dict(lse=None), _lib.ATTN_JVP_ERR_NULL),
+    (dict(d_o=None), _lib.ATTN_JVP_ERR_NULL),
+    (dict(dk=None), _lib.ATTN_JVP_ERR_UNSUPPORTED),
+    (dict(dq=None, dv=None), _lib.ATTN_JVP_ERR_UNSUPPORTED),
+    (dict(D=96), _lib.ATTN_JVP_ERR_UNSUPPORTED),
+    (dict(B=0), _lib.ATTN_JVP_ERR_SHAPE),
+    (dict(H=-1), _lib.ATTN_JVP_ERR_SHAPE),
+    (dict(n_q=37), _lib.ATTN_JVP_ERR_MASK),
+    (dict(n_k=11), _lib.ATTN_JVP_ERR_MASK),
+    (dict(q=0x10002), _lib.ATTN_JVP_ERR_ALIGN),
+    (dict(lse=0x90004), _lib.ATTN_JVP_ERR_ALIGN),
+    (dict(d_o=0x80008), _lib.ATTN_JVP_ERR_ALIGN),
+    (dict(q_stride_n=257), _lib.ATTN_JVP_ERR_ALIGN),
+    (dict(k_stride_h=132), _lib.ATTN_JVP_ERR_ALIGN),
+    (dict(q_stride_h=64), _lib.ATTN_JVP_ERR_SHAPE),
+    (dict(k_stride_b=-8), _lib.ATTN_JVP_ERR_SHAPE),
+    (dict(o=0x10000), _lib.ATTN_JVP_ERR_UNSUPPORTED),      # output aliases q
+    (dict(d_o=0x70000), _lib.ATTN_JVP_ERR_UNSUPPORTED),    # d_o aliases o
+    (dict(scale=float("nan")), _lib.ATTN_JVP_ERR_SHAPE),
+    (dict(scale=float("inf")), _lib.ATTN_JVP_ERR_SHAPE),
+]
+
+
+@pytest.mark.parametrize("kw,status", BAD)
+def test_fwd_rejects_bad_arguments(kw, status):
+    mask = aj.attn_jvp_mask_tf(4, 16, 1)
+    assert _fwd(_args(mask, **kw), mask) == status
+
+
+def test_fwd_null_args_and_mask():
+    mask = aj.attn_jvp_mask_tf(4, 16, 1)
+    L = _lib.lib()
+    assert L.attn_jvp_fwd(None, mask.handle, None) == _lib.ATTN_JVP_ERR_NULL
+    a = _args(mask)
+    assert L.attn_jvp_fwd(ctypes.byref(a), None, None) == _lib.ATTN_JVP_ERR_NULL
+
+
+@pytest.mark.skipif(_gpu_present(), reason="needs a host without a HIP device")
+def test_fwd_without_device_reports_hip_error():
+    mask = aj.attn_jvp_mask_tf(4, 16, 1)
+    assert _fwd(_args(mask), mask) == _lib.ATTN_JVP_ERR_HIP
+    assert _fwd(_args(mask, dq=None, dk=None, dv=None, d_o=None), mask) == _lib.ATTN_JVP_ERR_HIP
+
+
+def test_python_binding_requires_gpu_tensors():
+    import torch
+    mask = aj.attn_jvp_mask_tf(2, 4, 1)
+    x = torch.zeros(1, 16, 1, 64)
+    with pytest.raises(ValueError):
+        aj.attn_jvp_fwd(x, x, x, x, x, x, mask)
+    with pytest.raises(ValueError):
+        aj.attn_jvp_fwd(x, x, x, x, None, x, mask)

@@ -1,0 +1,335 @@
+"""GPU parity of the HIP path (through the C ABI) against the fp64 oracle.
+
+Tolerances (per output tensor O, dO, LSE): max|gpu - ref| <= tol * max|ref|,
+tol = 2e-2 for bf16 inputs and 1e-5 for fp32 inputs; every output finite
+where the reference is.  Inputs are seeded; the oracle sees the exact values
+the GPU sees (bf16 and fp32 widen to fp64 exactly).
+"""
+
+import math
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import attention_jvp_causal_attn_amd as aj
+from attention_jvp_causal_attn_amd.inputs import WORKLOADS, make_inputs, make_random
+from oracle import (dense_allowed, masked_attention, masked_attention_jvp, rects_allowed,
+                    tf_allowed)
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.bfloat16: 2e-2, torch.float32: 1e-5}
+DEV = "cuda"
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(x):
+    return {k: v.to(DEV) for k, v in x.items()}
+
+
+def run(xd, mask, tangent=True, scale=None):
+    if tangent:
+        o, do, lse = aj.attn_jvp_fwd(xd["q"], xd["k"], xd["v"], xd["dq"], xd["dk"], xd["dv"],
+                                     mask, scale=scale)
+    else:
+        o, do, lse = aj.attn_jvp_fwd(xd["q"], xd["k"], xd["v"], None, None, None, mask,
+                                     scale=scale)
+    torch.cuda.synchronize()
+    return o, do, lse
+
+
+def f64(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def check(name, got, ref, tol):
+    got = np.asarray(got, dtype=np.float64)
+    fin = np.isfinite(ref)
+    assert np.array_equal(np.isfinite(got), fin), f"{name}: finite pattern differs"
+    if not fin.any():
+        return 0.0
+    err = np.abs(got[fin] - ref[fin]).max()
+    scale = np.abs(ref[fin]).max()
+    rel = err / scale if scale > 0 else err
+    say(f"  {name}: max|err| = {err:.3e}, max|ref| = {scale:.3e}, ratio = {rel:.3e} (tol {tol})")
+    assert rel <= tol, f"{name}: {rel:.3e} > {tol}"
+    return rel
+
+
+def parity(x, pred, mask, tol, rows=None, scale=None):
+    xd = to_dev(x)
+    o, do, lse = run(xd, mask, scale=scale)
+    O, dO, LSE = masked_attention_jvp(x["q"], x["k"], x["v"], x["dq"], x["dk"], x["dv"], pred,
+                                      scale=scale, rows=rows)
+    sel = slice(None) if rows is None else torch.as_tensor(rows)
+    check("O", f64(o[:, sel]), O, tol)
+    check("dO", f64(do[:, sel]), dO, tol)
+    check("LSE", f64(lse[:, :, sel]), LSE, tol)
+    return o, do, lse
+
+
+# ------------------------------------------------------------ fp32 path ----
+
+def test_tiny_tf_fp32_workload():
+    w = WORKLOADS[1]
+    say(f"case: {w.describe()}")
+    x = make_inputs(w)
+    parity(x, tf_allowed(w.n_frames, w.tokens_per_frame, w.frames_per_chunk),
+           aj.attn_jvp_mask_tf(w.n_frames, w.tokens_per_frame, w.frames_per_chunk),
+           TOL[torch.float32])
+
+
+@pytest.mark.parametrize("nf,tpf,fpc,B,H,D", [(5, 37, 1, 2, 3, 128), (3, 21, 3, 1, 2, 64),
+                                              (2, 1, 1, 1, 1, 64)])
+def test_small_tf_fp32(nf, tpf, fpc, B, H, D):
+    say(f"case: fp32 TF nf={nf} tpf={tpf} fpc={fpc} B={B} H={H} D={D}")
+    pred = tf_allowed(nf, tpf, fpc)
+    x = make_random(B, pred.n_q, H, D, dtype="f32", seed=7000 + nf * 10 + D)
+    parity(x, pred, aj.attn_jvp_mask_tf(nf, tpf, fpc), TOL[torch.float32])
+
+
+# ------------------------------------------------------------ bf16 path ----
+
+SMALL_BF16 = [
+    (5, 37, 1, 2, 3, 128),   # N=370: 3 query tiles, ragged tail, unaligned units
+    (6, 23, 2, 1, 2, 64),    # chunk-wise, D=64
+    (4, 64, 1, 1, 2, 128),   # tile-aligned units
+    (3, 100, 3, 2, 1, 128),  # one chunk of 300 tokens per stream
+    (2, 1, 1, 1, 1, 128),    # N=4: rows with a single admissible key
+    (7, 50, 1, 1, 2, 64),
+    (9, 33, 3, 1, 1, 128),
+]
+
+
+@pytest.mark.parametrize("nf,tpf,fpc,B,H,D", SMALL_BF16)
+def test_small_tf_bf16(nf, tpf, fpc, B, H, D):
+    say(f"case: bf16 TF nf={nf} tpf={tpf} fpc={fpc} B={B} H={H} D={D}")
+    pred = tf_allowed(nf, tpf, fpc)
+    x = make_random(B, pred.n_q, H, D, dtype="bf16", seed=8000 + nf * 10 + D, tangent_std=0.1)
+    parity(x, pred, aj.attn_jvp_mask_tf(nf, tpf, fpc), TOL[torch.bfloat16])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_dense_and_rect_masks(dtype):
+    td = torch.bfloat16 if dtype == "bf16" else torch.float32
+    say(f"case: dense mask 200x200 {dtype}")
+    x = make_random(1, 200, 2, 128, dtype=dtype, seed=9100, tangent_std=0.2)
+    parity(x, dense_allowed(200, 200), aj.attn_jvp_mask_dense(200, 200), TOL[td], scale=0.05)
+    # generic rectangles, including rows with no admissible key at all
+    say(f"case: rect mask 150x150 {dtype}")
+    gq = [0, 10, 70, 100, 150]
+    rp = [0, 2, 3, 3, 5]
+    kb = [5, 40, 0, 0, 120]
+    ke = [20, 41, 150, 64, 150]
+    rects = [(gq[g], gq[g + 1], kb[r], ke[r]) for g in range(4) for r in range(rp[g], rp[g + 1])]
+    x = make_random(2, 150, 1, 64, dtype=dtype, seed=9200, tangent_std=0.1)
+    o, do, lse = parity(x, rects_allowed(150, 150, rects),
+                        aj.attn_jvp_mask_rects(150, 150, gq, rp, kb, ke), TOL[td])
+    assert torch.all(o[:, 70:100] == 0) and torch.all(do[:, 70:100] == 0)
+    assert torch.all(torch.isneginf(lse[:, :, 70:100]))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_queries_differ_from_keys(dtype):
+    # n_q != n_k: a chunk of 80 queries attending to 300 cached + own keys
+    td = torch.bfloat16 if dtype == "bf16" else torch.float32
+    n_q, n_k, H, D = 80, 380, 2, 128
+    say(f"case: rect n_q={n_q} n_k={n_k} {dtype}")
+    xq = make_random(1, n_q, H, D, dtype=dtype, seed=9300, tangent_std=0.1)
+    xk = make_random(1, n_k, H, D, dtype=dtype, seed=9400, tangent_std=0.1)
+    x = dict(q=xq["q"], dq=xq["dq"], k=xk["k"], v=xk["v"], dk=xk["dk"], dv=xk["dv"])
+    gq, rp, kb, ke = [0, 40, 80], [0, 1, 2], [0, 0], [340, 380]
+    pred = rects_allowed(n_q, n_k, [(0, 40, 0, 340), (40, 80, 0, 380)])
+    parity(x, pred, aj.attn_jvp_mask_rects(n_q, n_k, gq, rp, kb, ke), TOL[td])
+
+
+# ------------------------------------------------- invariants and modes ----
+
+def _tf_case(dtype="bf16", nf=6, tpf=29, fpc=2, B=1, H=2, D=128, seed=9500):
+    pred = tf_allowed(nf, tpf, fpc)
+    x = make_random(B, pred.n_q, H, D, dtype=dtype, seed=seed, tangent_std=0.1)
+    return pred, aj.attn_jvp_mask_tf(nf, tpf, fpc), x
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_primal_only_matches_jvp_primal(dtype):
+    pred, mask, x = _tf_case(dtype)
+    xd = to_dev(x)
+    o1, _, l1 = run(xd, mask, tangent=True)
+    o2, d2, l2 = run(xd, mask, tangent=False)
+    assert d2 is None
+    same = torch.equal(o1, o2) and torch.equal(l1, l2)
+    say(f"  primal-only O/LSE bitwise equal to the JVP run: {same}")
+    td = xd["q"].dtype
+    O, LSE = masked_attention(x["q"], x["k"], x["v"], pred)
+    check("O(primal)", f64(o2), O, TOL[td])
+    check("LSE(primal)", f64(l2), LSE, TOL[td])
+    check("O(primal vs jvp)", f64(o2), f64(o1), TOL[td])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_deterministic(dtype):
+    _, mask, x = _tf_case(dtype, seed=9600)
+    xd = to_dev(x)
+    a = run(xd, mask)
+    b = run(xd, mask)
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_rows_blind_to_inadmissible_keys(dtype):
+    # Rows of chunk 0 (clean and noisy) must be bitwise unchanged when K, V, dK,
+    # dV of every later-chunk token change (a noisy token's output does not
+    # depend on later chunks).
+    pred, mask, x = _tf_case(dtype, nf=6, tpf=29, fpc=2, seed=9700)
+    xd = to_dev(x)
+    base = run(xd, mask)
+    Nc, C = pred.n_clean, pred.unit_tokens
+    later = torch.tensor([t for t in range(pred.n_k) if (t % Nc) // C >= 1])
+    y = {k: v.clone() for k, v in xd.items()}
+    for n in ("k", "v", "dk", "dv"):
+        y[n][:, later.to(DEV)] = (y[n][:, later.to(DEV)] * -3.0 + 1.5).to(y[n].dtype)
+    pert = run(y, mask)
+    rows0 = torch.tensor([t for t in range(pred.n_q) if (t % Nc) // C == 0], device=DEV)
+    assert torch.equal(base[0][:, rows0], pert[0][:, rows0])
+    assert torch.equal(base[1][:, rows0], pert[1][:, rows0])
+    assert torch.equal(base[2][:, :, rows0], pert[2][:, :, rows0])
+    # and the rows that can see them did change
+    assert not torch.equal(base[0], pert[0])
+
+
+def test_head_and_batch_permutation_is_bitwise():
+    pred, mask, x = _tf_case("bf16", B=2, H=3, seed=9800)
+    xd = to_dev(x)
+    a = run(xd, mask)
+    perm_h = torch.tensor([2, 0, 1], device=DEV)
+    y = {k: v[:, :, perm_h].flip(0).contiguous() for k, v in xd.items()}
+    b = run(y, mask)
+    assert torch.equal(a[0][:, :, perm_h].flip(0), b[0])
+    assert torch.equal(a[1][:, :, perm_h].flip(0), b[1])
+    assert torch.equal(a[2][:, perm_h].flip(0), b[2])
+
+
+def test_tangent_linearity():
+    _, mask, x = _tf_case("bf16", seed=9900)
+    xd = to_dev(x)
+    _, d1, _ = run(xd, mask)
+    y = dict(xd)
+    for n in ("dq", "dk", "dv"):
+        y[n] = (xd[n].float() * 2.0).to(xd[n].dtype)   # exact in bf16
+    _, d2, _ = run(y, mask)
+    check("dO(2t) vs 2 dO(t)", f64(d2), 2.0 * f64(d1), 1e-2)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_single_visible_key(dtype):
+    N, H, D = 100, 2, 128
+    td = torch.bfloat16 if dtype == "bf16" else torch.float32
+    mask = aj.attn_jvp_mask_rects(N, N, list(range(N + 1)), list(range(N + 1)),
+                                  list(range(N)), list(range(1, N + 1)))
+    x = make_random(1, N, H, D, dtype=dtype, seed=9950, tangent_std=0.1)
+    xd = to_dev(x)
+    o, do, lse = run(xd, mask, scale=0.125)
+    assert torch.equal(o, xd["v"])                           # p = 1 exactly
+    check("dO=dv", f64(do), f64(xd["dv"]), TOL[td])
+    ref = 0.125 * (f64(xd["q"]) * f64(xd["k"])).sum(-1).transpose(0, 2, 1)
+    check("LSE=s_jj", f64(lse), ref, TOL[td])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_zero_queries_uniform_weights(dtype):
+    pred, mask, x = _tf_case(dtype, seed=9960)
+    td = torch.bfloat16 if dtype == "bf16" else torch.float32
+    x["q"] = torch.zeros_like(x["q"])
+    x["dq"] = torch.zeros_like(x["dq"])
+    xd = to_dev(x)
+    o, do, lse = run(xd, mask)
+    M = pred.matrix()
+    cnt = M.sum(1)
+    for h in range(x["q"].shape[2]):
+        check(f"O=mean v (h{h})", f64(o)[0, :, h], (M @ f64(x["v"])[0, :, h]) / cnt[:, None], TOL[td])
+        check(f"dO=mean dv (h{h})", f64(do)[0, :, h], (M @ f64(x["dv"])[0, :, h]) / cnt[:, None],
+              TOL[td])
+        check(f"LSE=ln|J| (h{h})", f64(lse)[0, h], np.log(cnt), TOL[td])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_outputs_fully_written_and_in_bounds(dtype):
+    # NaN-poisoned outputs inside guard bands: every output element is written,
+    # nothing past the ends is touched.
+    pred, mask, x = _tf_case(dtype, nf=5, tpf=37, fpc=1, B=1, H=3, seed=9970)
+    xd = to_dev(x)
+    B, N, H, D = xd["q"].shape
+    td = xd["q"].dtype
+    G = 4096
+    ob = torch.full((B * N * H * D + 2 * G,), float("nan"), dtype=td, device=DEV)
+    db = torch.full_like(ob, float("nan"))
+    lb = torch.full((B * H * N + 2 * G,), float("nan"), dtype=torch.float32, device=DEV)
+    o = ob[G:G + B * N * H * D].view(B, N, H, D)
+    do = db[G:G + B * N * H * D].view(B, N, H, D)
+    lse = lb[G:G + B * H * N].view(B, H, N)
+    aj.attn_jvp_fwd(xd["q"], xd["k"], xd["v"], xd["dq"], xd["dk"], xd["dv"], mask, o=o, d_o=do,
+                    lse=lse)
+    torch.cuda.synchronize()
+    for buf in (ob, db, lb):
+        assert torch.isnan(buf[:G]).all() and torch.isnan(buf[-G:]).all()
+        assert torch.isfinite(buf[G:-G]).all()
+
+
+def test_strided_views_of_fused_buffers():
+    # Q/dQ/O/dO and K/V/dK/dV as views of fused [B, N, 3, H, D]-style buffers
+    pred = tf_allowed(4, 45, 1)
+    B, N, H, D = 1, pred.n_q, 2, 128
+    x = make_random(B, N, H, D, dtype="bf16", seed=9980, tangent_std=0.1)
+    fused_k = torch.empty(B, N, 4, H, D, dtype=torch.bfloat16, device=DEV)
+    fused_q = torch.empty(B, N, 4, H, D, dtype=torch.bfloat16, device=DEV)
+    for i, n in enumerate(("k", "v", "dk", "dv")):
+        fused_k[:, :, i] = x[n].to(DEV)
+    fused_q[:, :, 0] = x["q"].to(DEV)
+    fused_q[:, :, 1] = x["dq"].to(DEV)
+    q, dq, o, do = (fused_q[:, :, i] for i in range(4))
+    k, v, dk, dv = (fused_k[:, :, i] for i in range(4))
+    mask = aj.attn_jvp_mask_tf(4, 45, 1)
+    lse = torch.empty(B, H, N, dtype=torch.float32, device=DEV)
+    aj.attn_jvp_fwd(q, k, v, dq, dk, dv, mask, o=o, d_o=do, lse=lse)
+    torch.cuda.synchronize()
+    O, dO, LSE = masked_attention_jvp(x["q"], x["k"], x["v"], x["dq"], x["dk"], x["dv"], pred)
+    check("O", f64(o), O, 2e-2)
+    check("dO", f64(do), dO, 2e-2)
+    check("LSE", f64(lse), LSE, 2e-2)
+
+
+# ------------------------------------------- full-size workloads, sampled ----
+
+def sample_rows(w, n_random=48, seed=0):
+    """Unit-boundary rows of both streams, query-tile boundary rows, and random
+    rows."""
+    Nc, C = w.n_frames * w.tokens_per_frame, w.unit_tokens
+    rows = set()
+    for s in (0, Nc):
+        for u in range(w.n_units):
+            rows.update({s + u * C, s + u * C + C - 1})
+    rows.update({0, w.N - 1, 127, 128, 8191, 8192})
+    rng = np.random.default_rng(seed)
+    rows.update(rng.integers(0, w.N, size=n_random).tolist())
+    return np.array(sorted(r for r in rows if 0 <= r < w.N))
+
+
+@pytest.mark.parametrize("wid", [2, 3, 4, 5])
+def test_full_size_workload_sampled(wid):
+    w = WORKLOADS[wid]
+    say(f"case: workload {wid}: {w.describe()}")
+    x = make_inputs(w)
+    mask = aj.attn_jvp_mask_tf(w.n_frames, w.tokens_per_frame, w.frames_per_chunk)
+    pred = tf_allowed(w.n_frames, w.tokens_per_frame, w.frames_per_chunk)
+    rows = sample_rows(w, seed=wid)
+    say(f"  {len(rows)} sampled rows per (b, h)")
+    parity(x, pred, mask, TOL[torch.bfloat16], rows=rows)
