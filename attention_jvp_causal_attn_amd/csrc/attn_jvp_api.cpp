@@ -30,7 +30,9 @@ int device_schedule_locked(const attn_jvp_mask *m, int device, int BM, int BN,
   const size_t off_bytes = (hs->tile_offsets.size() * 4 + 15) & ~size_t(15);
   const size_t ord_bytes = (hs->tile_order.size() * 4 + 15) & ~size_t(15);
   const size_t ent_bytes = (n_entries * 8 + 15) & ~size_t(15);
-  const size_t bit_bytes = hs->partial_bits.size() * 4;
+  // partial blocks, then one all-ones block that full blocks point at
+  const size_t ones_words = size_t(BM) * (BN / 32);
+  const size_t bit_bytes = (hs->partial_bits.size() + ones_words) * 4;
   const size_t total = off_bytes + ord_bytes + ent_bytes + bit_bytes + 16;
   std::vector<uint8_t> blob;
   try {
@@ -45,8 +47,10 @@ int device_schedule_locked(const attn_jvp_mask *m, int device, int BM, int BN,
     ent[2 * e] = hs->entry_block[e];
     ent[2 * e + 1] = hs->entry_partial[e];
   }
-  if (bit_bytes)
-    std::memcpy(blob.data() + off_bytes + ord_bytes + ent_bytes, hs->partial_bits.data(), bit_bytes);
+  uint8_t *bits_dst = blob.data() + off_bytes + ord_bytes + ent_bytes;
+  if (!hs->partial_bits.empty())
+    std::memcpy(bits_dst, hs->partial_bits.data(), hs->partial_bits.size() * 4);
+  std::memset(bits_dst + hs->partial_bits.size() * 4, 0xff, ones_words * 4);
   void *dptr = nullptr;
   hipError_t err = hipMalloc(&dptr, total);
   if (err == hipErrorOutOfMemory) return ATTN_JVP_ERR_OOM;
@@ -64,6 +68,7 @@ int device_schedule_locked(const attn_jvp_mask *m, int device, int BM, int BN,
   ds.entries = reinterpret_cast<const int2 *>(b + off_bytes + ord_bytes);
   ds.partial_bits = reinterpret_cast<const uint32_t *>(b + off_bytes + ord_bytes + ent_bytes);
   ds.n_tiles = hs->n_tiles;
+  ds.n_partial = int32_t(hs->n_partial);
   auto res = m->dev_sched.emplace(key, ds);
   *out = &res.first->second;
   return ATTN_JVP_OK;
@@ -158,6 +163,7 @@ extern "C" int attn_jvp_fwd(const attn_jvp_args *a, const attn_jvp_mask *m, void
   p.entries = ds->entries;
   p.partial_bits = ds->partial_bits;
   p.n_tiles = ds->n_tiles;
+  p.n_partial = ds->n_partial;
   int err = a->dtype == ATTN_JVP_BF16 ? attnjvp::launch_bf16(p, a->D, tangent, stream)
                                        : attnjvp::launch_f32(p, a->D, tangent, stream);
   return err == hipSuccess ? ATTN_JVP_OK : ATTN_JVP_ERR_HIP;

@@ -4,31 +4,36 @@
 // Appendix B: the tangent rides the primal FlashAttention pass with shared
 // rescaling, masked pairs carry no tangent, one sparse schedule of admissible
 // key blocks serves the primal and the tangent scores).  Per query row the
-// pass keeps the running max m, the sum l of exp(s - m), the sum mu of
+// pass keeps a reference max m, the sum l of exp(s - m), the sum mu of
 // exp(s - m) * ds, and two D-wide accumulators
 //     A = sum exp(s - m) v,   T = sum exp(s - m) (ds v + dv),
-// all rescaled by the same factor exp(m_old - m_new) when m grows, and ends
+// all rescaled by the same factor exp(m_old - m_new) when m moves, and ends
 // with O = A / l, dO = T / l - O * (mu / l), LSE = m + ln l.
 //
 // Work decomposition (MI355X-first):
 //  * one workgroup = 4 waves = 128 query rows of one (batch, head); each wave
-//    owns 32 rows, one lane per row in each half-wave, so per-row softmax
-//    state lives in a lane and only the two half-waves need a swap;
+//    owns 32 rows, one lane per row in each half-wave, so the per-row softmax
+//    state lives in a lane and only the two half-waves exchange the row max;
 //  * scores are computed transposed, S^T = K Q^T and dS^T = K dQ^T + dK Q^T,
 //    with v_mfma_f32_32x32x16_bf16: K / dK come from LDS as the A operand, Q
 //    and dQ stay in registers as the B operand for the whole key loop;
 //  * the accumulators are transposed too, A^T += V^T P^T and
 //    T^T += V^T (P*dS)^T + dV^T P^T, so the MFMA output of the score step is
-//    already the B operand of the value step (no shuffle of P);
-//  * V and dV are transposed once while being staged into LDS (4 keys x 8
-//    dims per thread, repacked in registers), so every MFMA operand read is a
-//    single 16-byte LDS load; K rows are read in a permuted order (bits 2 and
-//    3 of the row swapped) so that each lane's 8 probabilities of a 16-key
-//    step are 8 consecutive keys of V^T;
-//  * key blocks of 32 are double-buffered in LDS; the next block's global
-//    loads are in flight while the current block is computed;
-//  * full blocks run without any mask arithmetic; partial blocks read one
-//    32-bit word of admissible-key bits per row;
+//    already the B operand of the value step (no shuffle of P); K rows are
+//    read in a permuted order (bits 2 and 3 of the row swapped) so that each
+//    lane's 8 probabilities of a 16-key step are 8 consecutive keys;
+//  * V and dV stay row-major in LDS; the transposed V^T operand comes from
+//    ds_read_b64_tr_b16 (each group of 16 lanes turns 4 keys x 16 dims into
+//    16 lanes x 4 keys);
+//  * key blocks of 32 rows of K, dK, V, dV (and the admissible-key bits of
+//    partial blocks) go HBM -> LDS with direct-to-LDS loads through a
+//    3-stage ring, two blocks ahead of the MFMAs, without staging registers;
+//    each tile is XOR-swizzled in 16-byte chunks so the MFMA operand reads hit
+//    distinct banks;
+//  * the reference max moves only when a row max exceeds it by more than
+//    2^8 (a rare, wave-uniform branch), so the accumulators are not touched
+//    by vector ALU work in the steady state; p = exp2(s - m) then stays below
+//    2^8, far inside fp32 and bf16 range;
 //  * workgroups are renumbered so that the ones the dispatcher places on one
 //    XCD are consecutive tiles of the same (batch, head), heaviest first:
 //    they stream the same key blocks through that XCD's L2.
@@ -40,15 +45,29 @@ namespace attnjvp {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kThreads = 256;
+constexpr int kWaves = 4;
 constexpr int BM = kBf16BlockM;  // 128 query rows per workgroup
 constexpr int BN = kBf16BlockN;  // 32 keys per block
+constexpr int kStages = 3;
 static_assert(BM == 128 && BN == 32, "kernel layout assumes 4 waves x 32 rows, 32-key blocks");
 
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kRescaleSlack = 8.0f;  // log2 units: p <= 2^8 between rescales
+constexpr int kEntChunk = 512;        // schedule entries staged in LDS at a time
+
+template <int D>
+struct alignas(16) StageTile {
+  uint4 k[BN * D / 8];
+  uint4 dk[BN * D / 8];
+  uint4 v[BN * D / 8];
+  uint4 dv[BN * D / 8];
+  uint32_t bits[BM];
+};
 
 // Position of K row m of the 32x32 score tile: bits 2 and 3 swapped.  The
 // MFMA output element (row 8j + 4h + i) then holds key 16(j/2) + 8h + 4(j%2) + i,
@@ -57,16 +76,16 @@ __device__ __forceinline__ int swap_bits23(int m) {
   return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
 }
 
-// 16-byte-chunk XOR swizzles of the LDS tiles (bank spread for the MFMA
-// operand reads, where 16 or 32 lanes read one chunk column of many rows).
+// XOR swizzles of 16-byte chunks within a key row.
+// K / dK: the 16 lanes of one read touch 16 different rows at one chunk.
 template <int D>
-__device__ __forceinline__ int k_chunk(int row, int c) {
-  constexpr int KCH = D / 8;
-  return row * KCH + (c ^ ((row ^ (row >> 3)) & (KCH - 1)));
+__device__ __forceinline__ int k_swz(int row) {
+  return D == 128 ? (row & 15) : ((row >> 1) & 7);
 }
-__device__ __forceinline__ int vt_chunk(int d, int c) {
-  constexpr int VCH = BN / 8;  // 4 chunks per V^T row
-  return d * VCH + (c ^ (((d >> 1) ^ (d >> 3)) & (VCH - 1)));
+// V / dV: a transposed read touches 4 consecutive rows x 4 consecutive chunks.
+template <int D>
+__device__ __forceinline__ int v_swz(int row) {
+  return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 x) { return __builtin_bit_cast(bf16x8, x); }
@@ -87,6 +106,27 @@ __device__ __forceinline__ bf16x8 to_bf16x8(const float *x) {
 
 __device__ __forceinline__ float xor32(float v) { return __shfl_xor(v, 32, 64); }
 
+// 16 bytes per lane from global memory straight into LDS at lds_wave + 16 * lane
+// (lds_wave must be wave-uniform).  Tracked by vmcnt; the kernel waits for it
+// explicitly before the barrier that publishes a stage.
+__device__ __forceinline__ void dma16(const void *gptr, uint32_t lds_wave) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gptr), "s"(lds_wave)
+               : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(N), other counters untouched (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p)));
+}
+
 // Workgroup w is dispatched to XCD w % 8.  Renumber so that each XCD receives
 // a contiguous range of logical work items.
 __device__ __forceinline__ int xcd_logical(int w, int G) {
@@ -95,158 +135,120 @@ __device__ __forceinline__ int xcd_logical(int w, int G) {
   return xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
 }
 
-template <int D>
-struct Stage {
-  // Per-thread registers holding one key block on its way to LDS.
-  static constexpr int KCH = D / 8;                     // chunks per K row
-  static constexpr int K_CHUNKS = BN * KCH;             // per tensor
-  static constexpr int K_PER_THREAD = (K_CHUNKS + kThreads - 1) / kThreads;
-  static constexpr int V_UNITS = (BN / 4) * KCH;        // 4 keys x 8 dims
-  static constexpr int V_PER_THREAD = (2 * V_UNITS + kThreads - 1) / kThreads;
-  static_assert(K_CHUNKS % kThreads == 0, "K staging must tile the workgroup");
-  static_assert(V_PER_THREAD == 1, "one V or dV unit per thread");
-  uint4 k[K_PER_THREAD], dk[K_PER_THREAD];
-  uint4 v[4];
+template <int D, bool TAN>
+struct Dma {
+  static constexpr int KCH = D / 8;                 // 16-byte chunks per key row
+  static constexpr int CHUNKS = BN * KCH;           // per tensor tile
+  static constexpr int PER_TENSOR = CHUNKS / kThreads;
+  static constexpr int PER_STAGE = (TAN ? 4 : 2) * PER_TENSOR + 1;  // + mask bits
+  static_assert(CHUNKS % kThreads == 0, "tiles must be whole workgroup loads");
+  static_assert(BM * 4 == kWaves * 8 * 16, "mask bits: 8 lanes x 16 bytes per wave");
 };
 
+// Issue the direct-to-LDS loads of one key block (keys key0 .. key0+BN-1,
+// clamped to the last key: rows past n_k are masked out by the schedule).
 template <int D, bool TAN>
-__device__ __forceinline__ void load_block(Stage<D> &st, const KernelParams &p,
-                                           const __bf16 *kb_, const __bf16 *dkb_,
-                                           const __bf16 *vb_, const __bf16 *dvb_, int key0) {
-  constexpr int KCH = D / 8;
-  const int tid = threadIdx.x;
+__device__ __forceinline__ void issue_block(StageTile<D> *st, const KernelParams &p,
+                                            const __bf16 *kb_, const __bf16 *dkb_,
+                                            const __bf16 *vb_, const __bf16 *dvb_, int key0,
+                                            const uint32_t *bits_src) {
+  using M = Dma<D, TAN>;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-  for (int i = 0; i < Stage<D>::K_PER_THREAD; ++i) {
-    const int id = tid + i * kThreads;
-    const int row = id / KCH, c = id % KCH;
-    const int key = key0 + row;
-    uint4 z = {0u, 0u, 0u, 0u};
-    if (key < p.n_k) {
-      st.k[i] = *reinterpret_cast<const uint4 *>(kb_ + int64_t(key) * p.k_sn + c * 8);
-      if (TAN) st.dk[i] = *reinterpret_cast<const uint4 *>(dkb_ + int64_t(key) * p.k_sn + c * 8);
-    } else {
-      st.k[i] = z;
-      if (TAN) st.dk[i] = z;
+  for (int i = 0; i < M::PER_TENSOR; ++i) {
+    const int base = i * kThreads + wave * 64;  // first chunk of this wave-instruction
+    const int q = base + lane;
+    const int row = q / M::KCH, pch = q % M::KCH;
+    const int key = min(key0 + row, p.n_k - 1);
+    const int64_t roff = int64_t(key) * p.k_sn;
+    const int ck = pch ^ k_swz<D>(row), cv = pch ^ v_swz<D>(row);
+    dma16(kb_ + roff + ck * 8, lds_addr(&st->k[base]));
+    dma16(vb_ + roff + cv * 8, lds_addr(&st->v[base]));
+    if (TAN) {
+      dma16(dkb_ + roff + ck * 8, lds_addr(&st->dk[base]));
+      dma16(dvb_ + roff + cv * 8, lds_addr(&st->dv[base]));
     }
   }
-  // V / dV: thread u < V_UNITS handles V, the next V_UNITS handle dV.
-  const int u = tid;
-  if (u < 2 * Stage<D>::V_UNITS && (TAN || u < Stage<D>::V_UNITS)) {
-    const bool is_dv = u >= Stage<D>::V_UNITS;
-    const int uu = is_dv ? u - Stage<D>::V_UNITS : u;
-    const int kg = uu / KCH, c = uu % KCH;
-    const __bf16 *base = is_dv ? dvb_ : vb_;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int key = key0 + 4 * kg + r;
-      uint4 z = {0u, 0u, 0u, 0u};
-      st.v[r] = key < p.n_k ? *reinterpret_cast<const uint4 *>(base + int64_t(key) * p.k_sn + c * 8) : z;
-    }
-  }
+  // mask bits: BM words = 32 chunks; wave w copies chunks 8w .. 8w+7 (lanes 0..7)
+  if (lane < 8) dma16(bits_src + 4 * (wave * 8 + lane), lds_addr(&st->bits[32 * wave]));
 }
 
 template <int D, bool TAN>
-__device__ __forceinline__ void store_block(const Stage<D> &st, uint4 *lds) {
-  constexpr int KCH = D / 8;
-  constexpr int TILE = BN * D / 8;  // chunks per tensor tile
-  uint4 *Ks = lds, *dKs = lds + TILE, *Vt = lds + 2 * TILE, *dVt = lds + 3 * TILE;
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int i = 0; i < Stage<D>::K_PER_THREAD; ++i) {
-    const int id = tid + i * kThreads;
-    const int row = id / KCH, c = id % KCH;
-    Ks[k_chunk<D>(row, c)] = st.k[i];
-    if (TAN) dKs[k_chunk<D>(row, c)] = st.dk[i];
-  }
-  const int u = tid;
-  if (u < 2 * Stage<D>::V_UNITS && (TAN || u < Stage<D>::V_UNITS)) {
-    const bool is_dv = u >= Stage<D>::V_UNITS;
-    const int uu = is_dv ? u - Stage<D>::V_UNITS : u;
-    const int kg = uu / KCH, c = uu % KCH;
-    uint4 *dst = is_dv ? dVt : Vt;
-    // 4 keys x 8 dims -> 8 rows (dims) of 4 keys: rows 8c + e, keys 4kg..4kg+3
-    const uint32_t w[4][4] = {{st.v[0].x, st.v[0].y, st.v[0].z, st.v[0].w},
-                              {st.v[1].x, st.v[1].y, st.v[1].z, st.v[1].w},
-                              {st.v[2].x, st.v[2].y, st.v[2].z, st.v[2].w},
-                              {st.v[3].x, st.v[3].y, st.v[3].z, st.v[3].w}};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int wi = e >> 1;
-      uint32_t lo, hi;
-      if (e & 1) {
-        lo = (w[0][wi] >> 16) | (w[1][wi] & 0xffff0000u);
-        hi = (w[2][wi] >> 16) | (w[3][wi] & 0xffff0000u);
-      } else {
-        lo = (w[0][wi] & 0xffffu) | (w[1][wi] << 16);
-        hi = (w[2][wi] & 0xffffu) | (w[3][wi] << 16);
-      }
-      const int d = 8 * c + e;
-      uint2 *row = reinterpret_cast<uint2 *>(dst + vt_chunk(d, kg >> 1));
-      row[kg & 1] = make_uint2(lo, hi);
-    }
-  }
-}
-
-template <int D, bool TAN, bool PARTIAL>
-__device__ __forceinline__ void compute_block(const uint4 *lds, const bf16x8 *qf, const bf16x8 *dqf,
-                                              f32x16 *accO, f32x16 *accT, float &m_run, float &l_run,
-                                              float &mu_run, uint32_t bits, float scale_log2,
+__device__ __forceinline__ void compute_block(const StageTile<D> *st, const bf16x8 *qf,
+                                              const bf16x8 *dqf, f32x16 *accO, f32x16 *accT,
+                                              float &m_ref, float &l_run, float &mu_run,
+                                              bool partial, int row_in_tile, float scale_log2,
                                               float scale) {
   constexpr int KSTEPS = D / 16;
   constexpr int DT = D / 32;
-  constexpr int TILE = BN * D / 8;
-  const uint4 *Ks = lds, *dKs = lds + TILE, *Vt = lds + 2 * TILE, *dVt = lds + 3 * TILE;
+  constexpr int KCH = D / 8;
   const int lane = threadIdx.x & 63;
   const int col = lane & 31, hh = lane >> 5;
   const int krow = swap_bits23(col);
+  const uint4 *Ks = st->k + krow * KCH;
+  const uint4 *dKs = st->dk + krow * KCH;
+  const int kx = k_swz<D>(krow);
 
   f32x16 S = {}, dS = {};
 #pragma unroll
   for (int t = 0; t < KSTEPS; ++t) {
-    const int c = 2 * t + hh;
-    const bf16x8 kf = as_bf16x8(Ks[k_chunk<D>(krow, c)]);
+    const int c = (2 * t + hh) ^ kx;
+    const bf16x8 kf = as_bf16x8(Ks[c]);
     S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[t], S, 0, 0, 0);
     if (TAN) {
-      const bf16x8 dkf = as_bf16x8(dKs[k_chunk<D>(krow, c)]);
+      const bf16x8 dkf = as_bf16x8(dKs[c]);
       dS = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, dqf[t], dS, 0, 0, 0);
       dS = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dkf, qf[t], dS, 0, 0, 0);
     }
   }
 
-  float s[16];
-  float mx = kNegInf;
+  if (partial) {  // workgroup-uniform: only blocks that straddle a mask edge
+    const uint32_t bits = st->bits[row_in_tile];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int j = r >> 2, i = r & 3;
-    const int key = 16 * (j >> 1) + 8 * hh + 4 * (j & 1) + i;
-    bool ok = true;
-    if (PARTIAL) ok = (bits >> key) & 1u;
-    s[r] = ok ? S[r] * scale_log2 : kNegInf;
-    mx = fmaxf(mx, s[r]);
+    for (int r = 0; r < 16; ++r) {
+      const int j = r >> 2, i = r & 3;
+      const int key = 16 * (j >> 1) + 8 * hh + 4 * (j & 1) + i;
+      const bool ok = (bits >> key) & 1u;
+      S[r] = ok ? S[r] : kNegInf;
+      if (TAN) dS[r] = ok ? dS[r] : 0.f;
+    }
   }
-  mx = fmaxf(mx, xor32(mx));
-  const float m_new = fmaxf(m_run, mx);
-  const float m_use = m_new == kNegInf ? 0.f : m_new;
-  const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+
+  float mx = S[0];
+#pragma unroll
+  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[r]);
+  mx = fmaxf(mx, xor32(mx)) * scale_log2;
+  const bool grow = mx > m_ref + kRescaleSlack;
+  if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+    // Move the reference max (rare after the first block of a row).  Only the
+    // rows that crossed the slack move, so every row's arithmetic depends on
+    // its own admissible scores alone (alpha = 1 is exact for the others).
+    const float m_new = grow ? mx : m_ref;
+    const float alpha = grow ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.f;
+    l_run *= alpha;
+    mu_run *= alpha;
+#pragma unroll
+    for (int nt = 0; nt < DT; ++nt) {
+      accO[nt] *= alpha;
+      if (TAN) accT[nt] *= alpha;
+    }
+    m_ref = m_new;
+  }
+  const float m_use = m_ref == kNegInf ? 0.f : m_ref;
+
   float pr[16], pds[16];
   float lsum = 0.f, musum = 0.f;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    pr[r] = __builtin_amdgcn_exp2f(s[r] - m_use);
+    pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], scale_log2, -m_use));
     lsum += pr[r];
     if (TAN) {
-      const int j = r >> 2, i = r & 3;
-      const int key = 16 * (j >> 1) + 8 * hh + 4 * (j & 1) + i;
-      bool ok = true;
-      if (PARTIAL) ok = (bits >> key) & 1u;
-      const float ds = ok ? dS[r] * scale : 0.f;
-      pds[r] = pr[r] * ds;
+      pds[r] = pr[r] * (dS[r] * scale);
       musum += pds[r];
     }
   }
-  l_run = l_run * alpha + lsum;
-  if (TAN) mu_run = mu_run * alpha + musum;
-  m_run = m_new;
+  l_run += lsum;
+  if (TAN) mu_run += musum;
 
   bf16x8 pb[2], pdsb[2];
   pb[0] = to_bf16x8(pr);
@@ -255,23 +257,38 @@ __device__ __forceinline__ void compute_block(const uint4 *lds, const bf16x8 *qf
     pdsb[0] = to_bf16x8(pds);
     pdsb[1] = to_bf16x8(pds + 8);
   }
+
+  // Value step s covers keys 16s .. 16s+15; lane-half hh supplies keys
+  // 16s + 8hh + 0..7.  Transposed reads: within each 16-lane group, lane j
+  // points at key (16s + 8hh + 4*half + j/4), dims (d0 + 4*(j%4)) .. +3.
+  const int g = lane >> 4, jl = lane & 15;
+  const int dcol = 16 * (g & 1) + 4 * (jl & 3);  // + 32 * nt
+  const int krel = 8 * hh + (jl >> 2);            // + 16 * s + 4 * half
 #pragma unroll
-  for (int nt = 0; nt < DT; ++nt) {
-    accO[nt] *= alpha;
-    if (TAN) accT[nt] *= alpha;
-  }
-#pragma unroll
-  for (int st = 0; st < 2; ++st) {
-    const int c = 2 * st + hh;
+  for (int s = 0; s < 2; ++s) {
 #pragma unroll
     for (int nt = 0; nt < DT; ++nt) {
-      const int d = 32 * nt + col;
-      const bf16x8 vf = as_bf16x8(Vt[vt_chunk(d, c)]);
-      accO[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[st], accO[nt], 0, 0, 0);
+      const int d = 32 * nt + dcol;
+      bf16x4 vh[2], dvh[2];
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int key = 16 * s + 4 * half + krel;
+        const int chunk = key * KCH + ((d >> 3) ^ v_swz<D>(key));
+        const char *vp = reinterpret_cast<const char *>(st->v + chunk) + (d & 7) * 2;
+        vh[half] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (__attribute__((address_space(3))) bf16x4 *)(vp));
+        if (TAN) {
+          const char *dvp = reinterpret_cast<const char *>(st->dv + chunk) + (d & 7) * 2;
+          dvh[half] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (__attribute__((address_space(3))) bf16x4 *)(dvp));
+        }
+      }
+      const bf16x8 vf = __builtin_shufflevector(vh[0], vh[1], 0, 1, 2, 3, 4, 5, 6, 7);
+      accO[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[s], accO[nt], 0, 0, 0);
       if (TAN) {
-        const bf16x8 dvf = as_bf16x8(dVt[vt_chunk(d, c)]);
-        accT[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pdsb[st], accT[nt], 0, 0, 0);
-        accT[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dvf, pb[st], accT[nt], 0, 0, 0);
+        const bf16x8 dvf = __builtin_shufflevector(dvh[0], dvh[1], 0, 1, 2, 3, 4, 5, 6, 7);
+        accT[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pdsb[s], accT[nt], 0, 0, 0);
+        accT[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dvf, pb[s], accT[nt], 0, 0, 0);
       }
     }
   }
@@ -282,8 +299,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 void attn_jvp_bf16_kernel(KernelParams p) {
   constexpr int KSTEPS = D / 16;
   constexpr int DT = D / 32;
-  constexpr int TILE = BN * D / 8;
-  __shared__ uint4 smem[2 * 4 * TILE];
+  using M = Dma<D, TAN>;
+  __shared__ StageTile<D> ring[kStages];
 
   const int G = p.n_tiles * p.B * p.H;
   const int L = xcd_logical(int(blockIdx.x), G);
@@ -298,21 +315,57 @@ void attn_jvp_bf16_kernel(KernelParams p) {
   const int qrow = tile * BM + row_in_tile;
   const bool qvalid = qrow < p.n_q;
 
-  const __bf16 *qb = static_cast<const __bf16 *>(p.q) + int64_t(batch) * p.q_sb + int64_t(head) * p.q_sh;
-  const __bf16 *dqb = static_cast<const __bf16 *>(p.dq) + int64_t(batch) * p.q_sb + int64_t(head) * p.q_sh;
   const int64_t koff = int64_t(batch) * p.k_sb + int64_t(head) * p.k_sh;
   const __bf16 *kb_ = static_cast<const __bf16 *>(p.k) + koff;
   const __bf16 *vb_ = static_cast<const __bf16 *>(p.v) + koff;
   const __bf16 *dkb_ = TAN ? static_cast<const __bf16 *>(p.dk) + koff : nullptr;
   const __bf16 *dvb_ = TAN ? static_cast<const __bf16 *>(p.dv) + koff : nullptr;
 
-  bf16x8 qf[KSTEPS], dqf[KSTEPS];
+  const int e0 = p.tile_offsets[tile], e1 = p.tile_offsets[tile + 1];
+  const int n = e1 - e0;
+  // Schedule entries of this tile, staged in LDS in chunks (read with LDS
+  // loads inside the key loop, so no global load sits between the
+  // direct-to-LDS copies and the MFMAs).
+  __shared__ int2 ents[2][kEntChunk];
+  auto load_entries = [&](int c) {
+    int2 *dst = ents[c & 1];
+    const int base = e0 + c * kEntChunk;
 #pragma unroll
-  for (int t = 0; t < KSTEPS; ++t) {
-    uint4 z = {0u, 0u, 0u, 0u};
-    const int64_t off = int64_t(qrow) * p.q_sn + 16 * t + 8 * hh;
-    qf[t] = as_bf16x8(qvalid ? *reinterpret_cast<const uint4 *>(qb + off) : z);
-    if (TAN) dqf[t] = as_bf16x8(qvalid ? *reinterpret_cast<const uint4 *>(dqb + off) : z);
+    for (int i = threadIdx.x; i < kEntChunk; i += kThreads)
+      dst[i] = base + i < e1 ? p.entries[base + i] : make_int2(0, -1);
+  };
+  auto entry = [&](int j) { return ents[(j / kEntChunk) & 1][j % kEntChunk]; };
+  // Full blocks take their (all-ones) mask words from one extra block that
+  // the schedule keeps after the partial ones.
+  auto bits_of = [&](int2 ent) {
+    return p.partial_bits + int64_t(ent.y >= 0 ? ent.y : p.n_partial) * BM;
+  };
+
+  load_entries(0);
+  __syncthreads();
+  if (n > 0) {
+    const int2 ent0 = entry(0);
+    issue_block<D, TAN>(&ring[0], p, kb_, dkb_, vb_, dvb_, ent0.x * BN, bits_of(ent0));
+  }
+
+  bf16x8 qf[KSTEPS], dqf[KSTEPS];
+  {
+    const int qr = qvalid ? qrow : 0;
+    const int64_t off = int64_t(batch) * p.q_sb + int64_t(head) * p.q_sh + int64_t(qr) * p.q_sn + 8 * hh;
+    const __bf16 *qb = static_cast<const __bf16 *>(p.q) + off;
+    const __bf16 *dqb = TAN ? static_cast<const __bf16 *>(p.dq) + off : nullptr;
+#pragma unroll
+    for (int t = 0; t < KSTEPS; ++t) {
+      qf[t] = as_bf16x8(*reinterpret_cast<const uint4 *>(qb + 16 * t));
+      if (TAN) dqf[t] = as_bf16x8(*reinterpret_cast<const uint4 *>(dqb + 16 * t));
+    }
+  }
+  // Q, dQ and the first block are in before the loop: the loop itself then
+  // waits only on the direct-to-LDS copies.
+  wait_vmcnt<0>();
+  if (n > 1) {
+    const int2 ent1 = entry(1);
+    issue_block<D, TAN>(&ring[1], p, kb_, dkb_, vb_, dvb_, ent1.x * BN, bits_of(ent1));
   }
 
   f32x16 accO[DT], accT[DT];
@@ -321,31 +374,26 @@ void attn_jvp_bf16_kernel(KernelParams p) {
     accO[nt] = f32x16{};
     accT[nt] = f32x16{};
   }
-  float m_run = kNegInf, l_run = 0.f, mu_run = 0.f;
+  float m_ref = kNegInf, l_run = 0.f, mu_run = 0.f;
 
-  const int e0 = p.tile_offsets[tile], e1 = p.tile_offsets[tile + 1];
-  if (e0 < e1) {
-    Stage<D> st;
-    load_block<D, TAN>(st, p, kb_, dkb_, vb_, dvb_, p.entries[e0].x * BN);
-    store_block<D, TAN>(st, smem);
-    __syncthreads();
-    for (int e = e0; e < e1; ++e) {
-      const int stage = (e - e0) & 1;
-      const int2 ent = p.entries[e];
-      const bool has_next = e + 1 < e1;
-      if (has_next) load_block<D, TAN>(st, p, kb_, dkb_, vb_, dvb_, p.entries[e + 1].x * BN);
-      const uint4 *lds = smem + stage * 4 * TILE;
-      if (ent.y >= 0) {
-        const uint32_t bits = p.partial_bits[int64_t(ent.y) * BM + row_in_tile];
-        compute_block<D, TAN, true>(lds, qf, dqf, accO, accT, m_run, l_run, mu_run, bits,
-                                    p.scale_log2, p.scale);
-      } else {
-        compute_block<D, TAN, false>(lds, qf, dqf, accO, accT, m_run, l_run, mu_run, ~0u,
-                                     p.scale_log2, p.scale);
-      }
-      if (has_next) store_block<D, TAN>(st, smem + (stage ^ 1) * 4 * TILE);
-      __syncthreads();
+  int cur = 0;  // ring slot of block j
+  for (int j = 0; j < n; ++j) {
+    if ((j + 2) % kEntChunk == 0 && j + 2 < n) load_entries((j + 2) / kEntChunk);
+    if (j + 1 < n)
+      wait_vmcnt<M::PER_STAGE>();
+    else
+      wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (j + 2 < n) {
+      const int nxt = cur >= 1 ? cur - 1 : cur + 2;  // (cur + 2) % 3
+      const int2 ent2 = entry(j + 2);
+      issue_block<D, TAN>(&ring[nxt], p, kb_, dkb_, vb_, dvb_, ent2.x * BN, bits_of(ent2));
     }
+    const int2 ent = entry(j);
+    compute_block<D, TAN>(&ring[cur], qf, dqf, accO, accT, m_ref, l_run, mu_run, ent.y >= 0,
+                          row_in_tile, p.scale_log2, p.scale);
+    cur = cur == kStages - 1 ? 0 : cur + 1;
   }
 
   const float l_tot = l_run + xor32(l_run);
@@ -355,13 +403,11 @@ void attn_jvp_bf16_kernel(KernelParams p) {
   const float mu_n = mu_tot * inv;
   if (hh == 0) {
     p.lse[(int64_t(batch) * p.H + head) * p.n_q + qrow] =
-        l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : kNegInf;
+        l_tot > 0.f ? (m_ref + __log2f(l_tot)) * kLn2 : kNegInf;
   }
-  __bf16 *ob = static_cast<__bf16 *>(p.o) + int64_t(batch) * p.q_sb + int64_t(head) * p.q_sh +
-               int64_t(qrow) * p.q_sn;
-  __bf16 *dob = TAN ? static_cast<__bf16 *>(p.d_o) + int64_t(batch) * p.q_sb +
-                          int64_t(head) * p.q_sh + int64_t(qrow) * p.q_sn
-                    : nullptr;
+  const int64_t ooff = int64_t(batch) * p.q_sb + int64_t(head) * p.q_sh + int64_t(qrow) * p.q_sn;
+  __bf16 *ob = static_cast<__bf16 *>(p.o) + ooff;
+  __bf16 *dob = TAN ? static_cast<__bf16 *>(p.d_o) + ooff : nullptr;
 #pragma unroll
   for (int nt = 0; nt < DT; ++nt) {
 #pragma unroll

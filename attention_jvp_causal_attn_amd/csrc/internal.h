@@ -33,8 +33,9 @@ struct DeviceSchedule {
   const int32_t *tile_offsets = nullptr;
   const int32_t *tile_order = nullptr;
   const int2 *entries = nullptr;
-  const uint32_t *partial_bits = nullptr;
+  const uint32_t *partial_bits = nullptr;  // n_partial + 1 blocks; the last is all ones
   int32_t n_tiles = 0;
+  int32_t n_partial = 0;
 };
 
 // Everything a kernel launch needs, passed by value.
@@ -50,8 +51,9 @@ struct KernelParams {
   const int32_t *tile_offsets;
   const int32_t *tile_order;
   const int2 *entries;
-  const uint32_t *partial_bits;
+  const uint32_t *partial_bits;  // n_partial blocks, then one all-ones block
   int32_t n_tiles;
+  int32_t n_partial;
 };
 
 }  // namespace attnjvp
