@@ -39,6 +39,8 @@
 //    they stream the same key blocks through that XCD's L2.
 #include <hip/hip_runtime.h>
 
+#include <cstddef>
+
 #include "internal.h"
 
 namespace attnjvp {
@@ -90,29 +92,31 @@ __device__ __forceinline__ int v_swz(int row) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 x) { return __builtin_bit_cast(bf16x8, x); }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Round to nearest even, two values per v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  __bf16 a = static_cast<__bf16>(lo), b = static_cast<__bf16>(hi);
-  return uint32_t(__builtin_bit_cast(uint16_t, a)) | (uint32_t(__builtin_bit_cast(uint16_t, b)) << 16);
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 __device__ __forceinline__ bf16x8 to_bf16x8(const float *x) {
-  uint4 u;
-  u.x = pack_bf16(x[0], x[1]);
-  u.y = pack_bf16(x[2], x[3]);
-  u.z = pack_bf16(x[4], x[5]);
-  u.w = pack_bf16(x[6], x[7]);
-  return as_bf16x8(u);
+  const f32x8 v = {x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]};
+  return __builtin_convertvector(v, bf16x8);
 }
 
 __device__ __forceinline__ float xor32(float v) { return __shfl_xor(v, 32, 64); }
 
-// 16 bytes per lane from global memory straight into LDS at lds_wave + 16 * lane
-// (lds_wave must be wave-uniform).  Tracked by vmcnt; the kernel waits for it
-// explicitly before the barrier that publishes a stage.
-__device__ __forceinline__ void dma16(const void *gptr, uint32_t lds_wave) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+// 16 bytes per lane from global memory (wave-uniform base + per-lane byte
+// offset) straight into LDS at lds_wave + 16 * lane (lds_wave wave-uniform).
+// Tracked by vmcnt; the kernel waits for it explicitly before the barrier that
+// publishes a stage.
+__device__ __forceinline__ void dma16(const void *base, uint32_t voff, uint32_t lds_wave) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                :
-               : "v"(gptr), "s"(lds_wave)
+               : "v"(voff), "s"(base), "s"(lds_wave)
                : "memory", "m0");
 }
 
@@ -121,10 +125,6 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void *p) {
-  return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p)));
 }
 
 // Workgroup w is dispatched to XCD w % 8.  Renumber so that each XCD receives
@@ -145,32 +145,57 @@ struct Dma {
   static_assert(BM * 4 == kWaves * 8 * 16, "mask bits: 8 lanes x 16 bytes per wave");
 };
 
-// Issue the direct-to-LDS loads of one key block (keys key0 .. key0+BN-1,
-// clamped to the last key: rows past n_k are masked out by the schedule).
+// Per-lane byte offsets of the direct-to-LDS copies inside a key block: one
+// K-swizzled and one V-swizzled offset per wave-instruction.  Constant across
+// blocks (the block base moves in scalar registers).
 template <int D, bool TAN>
-__device__ __forceinline__ void issue_block(StageTile<D> *st, const KernelParams &p,
-                                            const __bf16 *kb_, const __bf16 *dkb_,
-                                            const __bf16 *vb_, const __bf16 *dvb_, int key0,
-                                            const uint32_t *bits_src) {
+struct DmaOffsets {
+  uint32_t k[Dma<D, TAN>::PER_TENSOR], v[Dma<D, TAN>::PER_TENSOR];
+};
+
+template <int D, bool TAN>
+__device__ __forceinline__ void dma_offsets(DmaOffsets<D, TAN> &o, int64_t k_sn, int rows_valid) {
   using M = Dma<D, TAN>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int i = 0; i < M::PER_TENSOR; ++i) {
-    const int base = i * kThreads + wave * 64;  // first chunk of this wave-instruction
-    const int q = base + lane;
+    const int q = i * kThreads + wave * 64 + lane;
     const int row = q / M::KCH, pch = q % M::KCH;
-    const int key = min(key0 + row, p.n_k - 1);
-    const int64_t roff = int64_t(key) * p.k_sn;
-    const int ck = pch ^ k_swz<D>(row), cv = pch ^ v_swz<D>(row);
-    dma16(kb_ + roff + ck * 8, lds_addr(&st->k[base]));
-    dma16(vb_ + roff + cv * 8, lds_addr(&st->v[base]));
+    // rows past the last key re-read the last key (masked out by the schedule)
+    const uint32_t roff = uint32_t(min(row, rows_valid - 1)) * uint32_t(k_sn) * 2u;
+    o.k[i] = roff + uint32_t(pch ^ k_swz<D>(row)) * 16u;
+    o.v[i] = roff + uint32_t(pch ^ v_swz<D>(row)) * 16u;
+  }
+}
+
+// Issue the direct-to-LDS loads of one key block starting at key key0 into
+// the stage tile at LDS byte address st (wave-uniform); wave is the
+// wave-uniform wave index.
+template <int D, bool TAN>
+__device__ __forceinline__ void issue_block(uint32_t st, int wave, const KernelParams &p,
+                                            const DmaOffsets<D, TAN> &full_off, const __bf16 *kb_,
+                                            const __bf16 *dkb_, const __bf16 *vb_,
+                                            const __bf16 *dvb_, int key0, const uint32_t *bits_src) {
+  using M = Dma<D, TAN>;
+  using T = StageTile<D>;
+  const int lane = threadIdx.x & 63;
+  const int64_t boff = int64_t(key0) * p.k_sn;
+  DmaOffsets<D, TAN> o = full_off;
+  if (key0 + BN > p.n_k) dma_offsets<D, TAN>(o, p.k_sn, p.n_k - key0);  // last block only
+#pragma unroll
+  for (int i = 0; i < M::PER_TENSOR; ++i) {
+    const uint32_t chunk = uint32_t(i * kThreads + wave * 64) * 16u;  // this wave-instruction
+    dma16(kb_ + boff, o.k[i], st + uint32_t(offsetof(T, k)) + chunk);
+    dma16(vb_ + boff, o.v[i], st + uint32_t(offsetof(T, v)) + chunk);
     if (TAN) {
-      dma16(dkb_ + roff + ck * 8, lds_addr(&st->dk[base]));
-      dma16(dvb_ + roff + cv * 8, lds_addr(&st->dv[base]));
+      dma16(dkb_ + boff, o.k[i], st + uint32_t(offsetof(T, dk)) + chunk);
+      dma16(dvb_ + boff, o.v[i], st + uint32_t(offsetof(T, dv)) + chunk);
     }
   }
   // mask bits: BM words = 32 chunks; wave w copies chunks 8w .. 8w+7 (lanes 0..7)
-  if (lane < 8) dma16(bits_src + 4 * (wave * 8 + lane), lds_addr(&st->bits[32 * wave]));
+  if (lane < 8)
+    dma16(bits_src, uint32_t(wave * 8 + lane) * 16u,
+          st + uint32_t(offsetof(T, bits)) + uint32_t(wave) * 128u);
 }
 
 template <int D, bool TAN>
@@ -309,9 +334,12 @@ void attn_jvp_bf16_kernel(KernelParams p) {
   const int head = bh % p.H, batch = bh / p.H;
   const int tile = p.tile_order[slot];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 31, hh = lane >> 5;
   const int row_in_tile = wave * 32 + col;
+  const uint32_t ring_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&ring[0]));
+  auto stage_lds = [&](int slot) { return ring_lds + uint32_t(slot) * uint32_t(sizeof(StageTile<D>)); };
   const int qrow = tile * BM + row_in_tile;
   const bool qvalid = qrow < p.n_q;
 
@@ -334,18 +362,23 @@ void attn_jvp_bf16_kernel(KernelParams p) {
     for (int i = threadIdx.x; i < kEntChunk; i += kThreads)
       dst[i] = base + i < e1 ? p.entries[base + i] : make_int2(0, -1);
   };
-  auto entry = [&](int j) { return ents[(j / kEntChunk) & 1][j % kEntChunk]; };
+  auto entry = [&](int j) {
+    const int2 e = ents[(j / kEntChunk) & 1][j % kEntChunk];
+    return make_int2(__builtin_amdgcn_readfirstlane(e.x), __builtin_amdgcn_readfirstlane(e.y));
+  };
   // Full blocks take their (all-ones) mask words from one extra block that
   // the schedule keeps after the partial ones.
   auto bits_of = [&](int2 ent) {
     return p.partial_bits + int64_t(ent.y >= 0 ? ent.y : p.n_partial) * BM;
   };
 
+  DmaOffsets<D, TAN> doff;
+  dma_offsets<D, TAN>(doff, p.k_sn, BN);
   load_entries(0);
   __syncthreads();
   if (n > 0) {
     const int2 ent0 = entry(0);
-    issue_block<D, TAN>(&ring[0], p, kb_, dkb_, vb_, dvb_, ent0.x * BN, bits_of(ent0));
+    issue_block<D, TAN>(stage_lds(0), wave, p, doff, kb_, dkb_, vb_, dvb_, ent0.x * BN, bits_of(ent0));
   }
 
   bf16x8 qf[KSTEPS], dqf[KSTEPS];
@@ -365,7 +398,7 @@ void attn_jvp_bf16_kernel(KernelParams p) {
   wait_vmcnt<0>();
   if (n > 1) {
     const int2 ent1 = entry(1);
-    issue_block<D, TAN>(&ring[1], p, kb_, dkb_, vb_, dvb_, ent1.x * BN, bits_of(ent1));
+    issue_block<D, TAN>(stage_lds(1), wave, p, doff, kb_, dkb_, vb_, dvb_, ent1.x * BN, bits_of(ent1));
   }
 
   f32x16 accO[DT], accT[DT];
@@ -388,7 +421,7 @@ void attn_jvp_bf16_kernel(KernelParams p) {
     if (j + 2 < n) {
       const int nxt = cur >= 1 ? cur - 1 : cur + 2;  // (cur + 2) % 3
       const int2 ent2 = entry(j + 2);
-      issue_block<D, TAN>(&ring[nxt], p, kb_, dkb_, vb_, dvb_, ent2.x * BN, bits_of(ent2));
+      issue_block<D, TAN>(stage_lds(nxt), wave, p, doff, kb_, dkb_, vb_, dvb_, ent2.x * BN, bits_of(ent2));
     }
     const int2 ent = entry(j);
     compute_block<D, TAN>(&ring[cur], qf, dqf, accO, accT, m_ref, l_run, mu_run, ent.y >= 0,

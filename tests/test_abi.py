@@ -88,6 +88,7 @@ BAD = [
     (dict(k_stride_h=132), _lib.ATTN_JVP_ERR_ALIGN),
     (dict(q_stride_h=64), _lib.ATTN_JVP_ERR_SHAPE),
     (dict(k_stride_b=-8), _lib.ATTN_JVP_ERR_SHAPE),
+    (dict(k_stride_n=1 << 25), _lib.ATTN_JVP_ERR_SHAPE),
     (dict(o=0x10000), _lib.ATTN_JVP_ERR_UNSUPPORTED),      # output aliases q
     (dict(d_o=0x70000), _lib.ATTN_JVP_ERR_UNSUPPORTED),    # d_o aliases o
     (dict(scale=float("nan")), _lib.ATTN_JVP_ERR_SHAPE),
