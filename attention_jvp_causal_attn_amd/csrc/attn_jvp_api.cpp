@@ -29,11 +29,12 @@ int device_schedule_locked(const attn_jvp_mask *m, int device, int BM, int BN,
   const size_t n_entries = hs->entry_block.size();
   const size_t off_bytes = (hs->tile_offsets.size() * 4 + 15) & ~size_t(15);
   const size_t ord_bytes = (hs->tile_order.size() * 4 + 15) & ~size_t(15);
+  const size_t nf_bytes = (hs->tile_nfull.size() * 4 + 15) & ~size_t(15);
   const size_t ent_bytes = (n_entries * 8 + 15) & ~size_t(15);
   // partial blocks, then one all-ones block that full blocks point at
   const size_t ones_words = size_t(BM) * (BN / 32);
   const size_t bit_bytes = (hs->partial_bits.size() + ones_words) * 4;
-  const size_t total = off_bytes + ord_bytes + ent_bytes + bit_bytes + 16;
+  const size_t total = off_bytes + ord_bytes + nf_bytes + ent_bytes + bit_bytes + 16;
   std::vector<uint8_t> blob;
   try {
     blob.assign(total, 0);
@@ -42,12 +43,14 @@ int device_schedule_locked(const attn_jvp_mask *m, int device, int BM, int BN,
   }
   std::memcpy(blob.data(), hs->tile_offsets.data(), hs->tile_offsets.size() * 4);
   std::memcpy(blob.data() + off_bytes, hs->tile_order.data(), hs->tile_order.size() * 4);
-  int32_t *ent = reinterpret_cast<int32_t *>(blob.data() + off_bytes + ord_bytes);
+  std::memcpy(blob.data() + off_bytes + ord_bytes, hs->tile_nfull.data(), hs->tile_nfull.size() * 4);
+  const size_t ent_at = off_bytes + ord_bytes + nf_bytes;
+  int32_t *ent = reinterpret_cast<int32_t *>(blob.data() + ent_at);
   for (size_t e = 0; e < n_entries; ++e) {
     ent[2 * e] = hs->entry_block[e];
     ent[2 * e + 1] = hs->entry_partial[e];
   }
-  uint8_t *bits_dst = blob.data() + off_bytes + ord_bytes + ent_bytes;
+  uint8_t *bits_dst = blob.data() + ent_at + ent_bytes;
   if (!hs->partial_bits.empty())
     std::memcpy(bits_dst, hs->partial_bits.data(), hs->partial_bits.size() * 4);
   std::memset(bits_dst + hs->partial_bits.size() * 4, 0xff, ones_words * 4);
@@ -65,8 +68,9 @@ int device_schedule_locked(const attn_jvp_mask *m, int device, int BM, int BN,
   ds.base = dptr;
   ds.tile_offsets = reinterpret_cast<const int32_t *>(b);
   ds.tile_order = reinterpret_cast<const int32_t *>(b + off_bytes);
-  ds.entries = reinterpret_cast<const int2 *>(b + off_bytes + ord_bytes);
-  ds.partial_bits = reinterpret_cast<const uint32_t *>(b + off_bytes + ord_bytes + ent_bytes);
+  ds.tile_nfull = reinterpret_cast<const int32_t *>(b + off_bytes + ord_bytes);
+  ds.entries = reinterpret_cast<const int2 *>(b + ent_at);
+  ds.partial_bits = reinterpret_cast<const uint32_t *>(b + ent_at + ent_bytes);
   ds.n_tiles = hs->n_tiles;
   ds.n_partial = int32_t(hs->n_partial);
   auto res = m->dev_sched.emplace(key, ds);
@@ -162,6 +166,7 @@ extern "C" int attn_jvp_fwd(const attn_jvp_args *a, const attn_jvp_mask *m, void
   p.scale_log2 = float(double(p.scale) * 1.4426950408889634);
   p.tile_offsets = ds->tile_offsets;
   p.tile_order = ds->tile_order;
+  p.tile_nfull = ds->tile_nfull;
   p.entries = ds->entries;
   p.partial_bits = ds->partial_bits;
   p.n_tiles = ds->n_tiles;

@@ -30,10 +30,11 @@
 //    3-stage ring, two blocks ahead of the MFMAs, without staging registers;
 //    each tile is XOR-swizzled in 16-byte chunks so the MFMA operand reads hit
 //    distinct banks;
-//  * the reference max moves only when a row max exceeds it by more than
-//    2^8 (a rare, wave-uniform branch), so the accumulators are not touched
-//    by vector ALU work in the steady state; p = exp2(s - m) then stays below
-//    2^8, far inside fp32 and bf16 range;
+//  * the MFMA accumulators live in AGPRs for the whole pass; the reference
+//    max moves only when a row max exceeds it by more than 2^8 (a rare,
+//    wave-uniform branch that multiplies the accumulators in place), so no
+//    vector ALU work touches them in the steady state; p = exp2(s - m) then
+//    stays below 2^8, far inside fp32 and bf16 range;
 //  * workgroups are renumbered so that the ones the dispatcher places on one
 //    XCD are consecutive tiles of the same (batch, head), heaviest first:
 //    they stream the same key blocks through that XCD's L2.
@@ -114,7 +115,8 @@ __device__ __forceinline__ float xor32(float v) { return __shfl_xor(v, 32, 64); 
 // Tracked by vmcnt; the kernel waits for it explicitly before the barrier that
 // publishes a stage.
 __device__ __forceinline__ void dma16(const void *base, uint32_t voff, uint32_t lds_wave) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+  // one wait state between the M0 write and the LDS-DMA that reads it
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :
                : "v"(voff), "s"(base), "s"(lds_wave)
                : "memory", "m0");
@@ -252,11 +254,24 @@ __device__ __forceinline__ void compute_block(const StageTile<D> *st, const bf16
     const float alpha = grow ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.f;
     l_run *= alpha;
     mu_run *= alpha;
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 #pragma unroll
     for (int nt = 0; nt < DT; ++nt) {
-      accO[nt] *= alpha;
-      if (TAN) accT[nt] *= alpha;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float x = accO[nt][i], tmp;
+        asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                     : "+a"(x), "=&v"(tmp) : "v"(alpha));
+        accO[nt][i] = x;
+        if (TAN) {
+          float y = accT[nt][i], tmp2;
+          asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                       : "+a"(y), "=&v"(tmp2) : "v"(alpha));
+          accT[nt][i] = y;
+        }
+      }
     }
+    asm volatile("s_nop 4" ::: "memory");
     m_ref = m_new;
   }
   const float m_use = m_ref == kNegInf ? 0.f : m_ref;

@@ -180,6 +180,7 @@ static void build_schedule(const attn_jvp_mask *m, int BM, int BN, HostSchedule 
   s.block_n = BN;
   s.n_tiles = n_tiles;
   s.tile_offsets.assign(1, 0);
+  s.tile_nfull.clear();
   s.entry_block.clear();
   s.entry_partial.clear();
   s.partial_bits.clear();
@@ -216,7 +217,16 @@ static void build_schedule(const attn_jvp_mask *m, int BM, int BN, HostSchedule 
         group_cnt[kb] = 0;
       }
     }
-    std::sort(touched.begin(), touched.end());
+    // Full blocks first (increasing), then partial blocks (increasing): the
+    // kernels run the full blocks in a software-pipelined loop without any
+    // mask arithmetic and the few partial ones after them.
+    std::sort(touched.begin(), touched.end(), [&](int a, int b) {
+      const bool fa = full_groups[a] == n_tile_groups, fb = full_groups[b] == n_tile_groups;
+      return fa != fb ? fa : a < b;
+    });
+    int32_t n_full = 0;
+    for (int kb : touched) n_full += full_groups[kb] == n_tile_groups;
+    s.tile_nfull.push_back(n_full);
     for (int kb : touched) {
       const bool full = full_groups[kb] == n_tile_groups;
       s.entry_block.push_back(kb);

@@ -42,11 +42,6 @@ def compile_one(src, verbose):
     cmd = [hipcc()] + COMMON + ["-c", os.path.join(HERE, src), "-o", obj]
     if src.endswith(".hip"):
         cmd[1:1] = ["-x", "hip"]
-    if src == "attn_jvp_bf16.hip":
-        # MFMA accumulators in VGPRs: the online-softmax rescale touches them
-        # with vector ALU ops, and AGPR-form accumulators would be copied
-        # between register files on every loop iteration.
-        cmd += ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -20,6 +20,7 @@ struct HostSchedule {
   int32_t n_tiles = 0;
   std::vector<int32_t> tile_offsets;   // n_tiles + 1
   std::vector<int32_t> tile_order;     // n_tiles, heaviest first
+  std::vector<int32_t> tile_nfull;     // n_tiles: full blocks lead each tile's entries
   std::vector<int32_t> entry_block;    // n_entries
   std::vector<int32_t> entry_partial;  // n_entries, -1 = full block
   std::vector<uint32_t> partial_bits;  // n_partial * block_m * (block_n / 32)
@@ -32,6 +33,7 @@ struct DeviceSchedule {
   void *base = nullptr;
   const int32_t *tile_offsets = nullptr;
   const int32_t *tile_order = nullptr;
+  const int32_t *tile_nfull = nullptr;
   const int2 *entries = nullptr;
   const uint32_t *partial_bits = nullptr;  // n_partial + 1 blocks; the last is all ones
   int32_t n_tiles = 0;
@@ -50,6 +52,7 @@ struct KernelParams {
   float scale_log2;   // scale * log2(e): scores go to exp2 directly
   const int32_t *tile_offsets;
   const int32_t *tile_order;
+  const int32_t *tile_nfull;
   const int2 *entries;
   const uint32_t *partial_bits;  // n_partial blocks, then one all-ones block
   int32_t n_tiles;

@@ -76,7 +76,7 @@ def time_calls(fn, steps, warmup, stream):
     return total / steps, per
 
 
-def cpu_baseline(w, x, target_s=15.0):
+def cpu_baseline(w, x, target_s=18.0):
     """The fp64 oracle on a bounded sample of the same workload: query rows of
     slice (b=0, h=0) spread over every unit of both streams, sized to about
     ``target_s`` seconds of host time; scaled to TFLOP/s with the same
@@ -101,10 +101,12 @@ def cpu_baseline(w, x, target_s=15.0):
                              rows=rows)
         return time.perf_counter() - t0, pairs, n_rows
 
-    dt, pairs, n = run(64)
-    if dt < target_s / 3:
-        n2 = int(min(w.N, max(64, 64 * target_s / max(dt, 1e-3))))
-        dt, pairs, n = run(n2)
+    dt, pairs, n = run(128)
+    for _ in range(3):  # grow the sample until it takes 10-30 s of host time
+        if dt >= 10.0 or n >= w.N:
+            break
+        n = int(min(w.N, max(n + 1, n * target_s / max(dt, 1e-3))))
+        dt, pairs, n = run(n)
     tflops = 12 * w.D * pairs / dt / 1e12
     return {"value": tflops, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": (f"fp64 numpy oracle on {n} random query rows of one (b,h) slice "

@@ -110,10 +110,11 @@ int attn_jvp_mask_export(const attn_jvp_mask *m, int32_t *group_q_begin,
 /* Host copy of the block schedule the kernels use for a tile shape
  * (block_m query rows x block_n keys, block_n a multiple of 32).  For query
  * tile t (rows [t*block_m, (t+1)*block_m)), entries tile_offsets[t] ..
- * tile_offsets[t+1]-1 list, in increasing order, the key blocks b (keys
- * [b*block_n, (b+1)*block_n)) holding at least one admissible pair of the
- * tile.  entry_partial[e] is -1 when every (row, key) of the block is
- * admissible for every row of the tile that exists, else an index p into
+ * tile_offsets[t+1]-1 list the key blocks b (keys [b*block_n, (b+1)*block_n))
+ * holding at least one admissible pair of the tile: first the full blocks in
+ * increasing order, then the partial ones in increasing order.
+ * entry_partial[e] is -1 for a full block (every (row, key) of the block is
+ * admissible for every row of the tile that exists), else an index p into
  * partial_bits, where word
  *   partial_bits[(p * block_m + r) * (block_n / 32) + w]
  * bit i says whether row t*block_m + r may see key b*block_n + 32*w + i.

@@ -112,7 +112,8 @@ def brute_schedule(M, BM, BN):
             blk[:, :sub.shape[1]] = sub
             if blk.any():
                 ents.append((kb, bool(blk.all()), blk))
-        out.append(ents)
+        # full blocks first, then partial ones, each in increasing order
+        out.append([e for e in ents if e[1]] + [e for e in ents if not e[1]])
     return out
 
 
