@@ -106,6 +106,27 @@ extern "C" int attn_jvp_tile_shape(int32_t dtype, int32_t D, int32_t *block_m, i
   return ATTN_JVP_OK;
 }
 
+// Workgroup -> work item map (see work_item in internal.h).  The 8 XCDs are
+// split into gcd(S, 8) groups sharing the S = B * H slices equally; the XCDs
+// of a group interleave the tile slots of each of its slices.  Needs the
+// slot count to split evenly over a group, else the identity map (which
+// interleaves slots over all 8 XCDs) is used.
+static void set_work_map(attnjvp::KernelParams &p) {
+  const int64_t S = int64_t(p.B) * p.H;
+  int64_t g = 8;
+  while (S % g != 0) g /= 2;
+  const int m = int(8 / g);
+  if (p.n_tiles % m == 0) {
+    p.map_group = m;
+    p.map_slices = int(S / g);
+    p.map_slots = p.n_tiles / m;
+  } else {
+    p.map_group = 0;
+    p.map_slices = 0;
+    p.map_slots = 0;
+  }
+}
+
 extern "C" int attn_jvp_fwd(const attn_jvp_args *a, const attn_jvp_mask *m, void *stream) {
   if (!a || !m) return ATTN_JVP_ERR_NULL;
   if (a->dtype != ATTN_JVP_BF16 && a->dtype != ATTN_JVP_F32) return ATTN_JVP_ERR_DTYPE;
@@ -171,6 +192,7 @@ extern "C" int attn_jvp_fwd(const attn_jvp_args *a, const attn_jvp_mask *m, void
   p.partial_bits = ds->partial_bits;
   p.n_tiles = ds->n_tiles;
   p.n_partial = ds->n_partial;
+  set_work_map(p);
   int err = a->dtype == ATTN_JVP_BF16 ? attnjvp::launch_bf16(p, a->D, tangent, stream)
                                        : attnjvp::launch_f32(p, a->D, tangent, stream);
   return err == hipSuccess ? ATTN_JVP_OK : ATTN_JVP_ERR_HIP;

@@ -35,9 +35,14 @@
 //    wave-uniform branch that multiplies the accumulators in place), so no
 //    vector ALU work touches them in the steady state; p = exp2(s - m) then
 //    stays below 2^8, far inside fp32 and bf16 range;
-//  * workgroups are renumbered so that the ones the dispatcher places on one
-//    XCD are consecutive tiles of the same (batch, head), heaviest first:
-//    they stream the same key blocks through that XCD's L2.
+//  * workgroups are mapped to work so that each XCD (the dispatcher sends
+//    workgroup w to XCD w % 8) receives an equal share of every group of
+//    (batch, head) slices, as interleaved heavy-first tile slots, while the
+//    workgroups resident on one XCD at a time belong to the same slice and
+//    stream the same key blocks through that XCD's L2 (work_item);
+//  * the copies of key block j + 2 go out once the score operands of block j
+//    have been read, so the score MFMAs start right after the barrier; the
+//    schedule entries of the next blocks ride in scalar registers.
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
@@ -129,14 +134,6 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Workgroup w is dispatched to XCD w % 8.  Renumber so that each XCD receives
-// a contiguous range of logical work items.
-__device__ __forceinline__ int xcd_logical(int w, int G) {
-  const int xcd = w & 7, local = w >> 3;
-  const int q = G >> 3, r = G & 7;
-  return xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
-}
-
 template <int D, bool TAN>
 struct Dma {
   static constexpr int KCH = D / 8;                 // 16-byte chunks per key row
@@ -200,14 +197,11 @@ __device__ __forceinline__ void issue_block(uint32_t st, int wave, const KernelP
           st + uint32_t(offsetof(T, bits)) + uint32_t(wave) * 128u);
 }
 
+// Score step of one key block: S^T = K Q^T and dS^T = K dQ^T + dK Q^T.
 template <int D, bool TAN>
-__device__ __forceinline__ void compute_block(const StageTile<D> *st, const bf16x8 *qf,
-                                              const bf16x8 *dqf, f32x16 *accO, f32x16 *accT,
-                                              float &m_ref, float &l_run, float &mu_run,
-                                              bool partial, int row_in_tile, float scale_log2,
-                                              float scale) {
+__device__ __forceinline__ void score_block(const StageTile<D> *st, const bf16x8 *qf,
+                                            const bf16x8 *dqf, f32x16 &S, f32x16 &dS) {
   constexpr int KSTEPS = D / 16;
-  constexpr int DT = D / 32;
   constexpr int KCH = D / 8;
   const int lane = threadIdx.x & 63;
   const int col = lane & 31, hh = lane >> 5;
@@ -216,7 +210,8 @@ __device__ __forceinline__ void compute_block(const StageTile<D> *st, const bf16
   const uint4 *dKs = st->dk + krow * KCH;
   const int kx = k_swz<D>(krow);
 
-  f32x16 S = {}, dS = {};
+  S = f32x16{};
+  dS = f32x16{};
 #pragma unroll
   for (int t = 0; t < KSTEPS; ++t) {
     const int c = (2 * t + hh) ^ kx;
@@ -228,6 +223,19 @@ __device__ __forceinline__ void compute_block(const StageTile<D> *st, const bf16
       dS = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dkf, qf[t], dS, 0, 0, 0);
     }
   }
+}
+
+// Masking, online-softmax update and value step of one key block.
+template <int D, bool TAN>
+__device__ __forceinline__ void softmax_value_block(const StageTile<D> *st, f32x16 S, f32x16 dS,
+                                                    f32x16 *accO, f32x16 *accT, float &m_ref,
+                                                    float &l_run, float &mu_run, bool partial,
+                                                    int row_in_tile, float scale_log2,
+                                                    float scale) {
+  constexpr int DT = D / 32;
+  constexpr int KCH = D / 8;
+  const int lane = threadIdx.x & 63;
+  const int hh = lane >> 5;
 
   if (partial) {  // workgroup-uniform: only blocks that straddle a mask edge
     const uint32_t bits = st->bits[row_in_tile];
@@ -241,15 +249,18 @@ __device__ __forceinline__ void compute_block(const StageTile<D> *st, const bf16
     }
   }
 
-  float mx = S[0];
+  // Max over this lane's 16 keys; the two half-waves exchange it only when
+  // one of them crosses the slack, since a row can grow only then.
+  float mh = S[0];
 #pragma unroll
-  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[r]);
-  mx = fmaxf(mx, xor32(mx)) * scale_log2;
-  const bool grow = mx > m_ref + kRescaleSlack;
-  if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+  for (int r = 1; r < 16; ++r) mh = fmaxf(mh, S[r]);
+  mh *= scale_log2;
+  if (__builtin_amdgcn_ballot_w64(mh > m_ref + kRescaleSlack) != 0) {
     // Move the reference max (rare after the first block of a row).  Only the
     // rows that crossed the slack move, so every row's arithmetic depends on
     // its own admissible scores alone (alpha = 1 is exact for the others).
+    const float mx = fmaxf(mh, xor32(mh));
+    const bool grow = mx > m_ref + kRescaleSlack;
     const float m_new = grow ? mx : m_ref;
     const float alpha = grow ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.f;
     l_run *= alpha;
@@ -283,8 +294,9 @@ __device__ __forceinline__ void compute_block(const StageTile<D> *st, const bf16
     pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], scale_log2, -m_use));
     lsum += pr[r];
     if (TAN) {
-      pds[r] = pr[r] * (dS[r] * scale);
-      musum += pds[r];
+      const float dss = dS[r] * scale;
+      pds[r] = pr[r] * dss;
+      musum = __builtin_fmaf(pr[r], dss, musum);
     }
   }
   l_run += lsum;
@@ -342,8 +354,7 @@ void attn_jvp_bf16_kernel(KernelParams p) {
   using M = Dma<D, TAN>;
   __shared__ StageTile<D> ring[kStages];
 
-  const int G = p.n_tiles * p.B * p.H;
-  const int L = xcd_logical(int(blockIdx.x), G);
+  const int L = work_item(int(blockIdx.x), p);
   const int slot = L % p.n_tiles;
   const int bh = L / p.n_tiles;
   const int head = bh % p.H, batch = bh / p.H;
@@ -391,10 +402,14 @@ void attn_jvp_bf16_kernel(KernelParams p) {
   dma_offsets<D, TAN>(doff, p.k_sn, BN);
   load_entries(0);
   __syncthreads();
-  if (n > 0) {
-    const int2 ent0 = entry(0);
-    issue_block<D, TAN>(stage_lds(0), wave, p, doff, kb_, dkb_, vb_, dvb_, ent0.x * BN, bits_of(ent0));
-  }
+  // Entries of blocks j, j + 1 and j + 2 ride in scalar registers; the one of
+  // block j + 3 is read from LDS during block j.
+  const int2 no_ent = make_int2(0, -1);
+  int2 ent_c = n > 0 ? entry(0) : no_ent;
+  int2 ent_1 = n > 1 ? entry(1) : no_ent;
+  int2 ent_2 = n > 2 ? entry(2) : no_ent;
+  if (n > 0)
+    issue_block<D, TAN>(stage_lds(0), wave, p, doff, kb_, dkb_, vb_, dvb_, ent_c.x * BN, bits_of(ent_c));
 
   bf16x8 qf[KSTEPS], dqf[KSTEPS];
   {
@@ -411,10 +426,8 @@ void attn_jvp_bf16_kernel(KernelParams p) {
   // Q, dQ and the first block are in before the loop: the loop itself then
   // waits only on the direct-to-LDS copies.
   wait_vmcnt<0>();
-  if (n > 1) {
-    const int2 ent1 = entry(1);
-    issue_block<D, TAN>(stage_lds(1), wave, p, doff, kb_, dkb_, vb_, dvb_, ent1.x * BN, bits_of(ent1));
-  }
+  if (n > 1)
+    issue_block<D, TAN>(stage_lds(1), wave, p, doff, kb_, dkb_, vb_, dvb_, ent_1.x * BN, bits_of(ent_1));
 
   f32x16 accO[DT], accT[DT];
 #pragma unroll
@@ -426,21 +439,27 @@ void attn_jvp_bf16_kernel(KernelParams p) {
 
   int cur = 0;  // ring slot of block j
   for (int j = 0; j < n; ++j) {
-    if ((j + 2) % kEntChunk == 0 && j + 2 < n) load_entries((j + 2) / kEntChunk);
+    if ((j + 3) % kEntChunk == 0 && j + 3 < n) load_entries((j + 3) / kEntChunk);
     if (j + 1 < n)
       wait_vmcnt<M::PER_STAGE>();
     else
       wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
+    const int2 raw3 = ents[((j + 3) / kEntChunk) & 1][(j + 3) % kEntChunk];
+    f32x16 S, dS;
+    score_block<D, TAN>(&ring[cur], qf, dqf, S, dS);
+    // The copies of block j + 2 go out after the score operands of block j
+    // have been read, so the score MFMAs start right after the barrier.
     if (j + 2 < n) {
       const int nxt = cur >= 1 ? cur - 1 : cur + 2;  // (cur + 2) % 3
-      const int2 ent2 = entry(j + 2);
-      issue_block<D, TAN>(stage_lds(nxt), wave, p, doff, kb_, dkb_, vb_, dvb_, ent2.x * BN, bits_of(ent2));
+      issue_block<D, TAN>(stage_lds(nxt), wave, p, doff, kb_, dkb_, vb_, dvb_, ent_2.x * BN, bits_of(ent_2));
     }
-    const int2 ent = entry(j);
-    compute_block<D, TAN>(&ring[cur], qf, dqf, accO, accT, m_ref, l_run, mu_run, ent.y >= 0,
-                          row_in_tile, p.scale_log2, p.scale);
+    softmax_value_block<D, TAN>(&ring[cur], S, dS, accO, accT, m_ref, l_run, mu_run, ent_c.y >= 0,
+                                row_in_tile, p.scale_log2, p.scale);
+    ent_c = ent_1;
+    ent_1 = ent_2;
+    ent_2 = make_int2(__builtin_amdgcn_readfirstlane(raw3.x), __builtin_amdgcn_readfirstlane(raw3.y));
     cur = cur == kStages - 1 ? 0 : cur + 1;
   }
 
@@ -465,7 +484,7 @@ void attn_jvp_bf16_kernel(KernelParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         o[i] = accO[nt][4 * j + i] * inv;
-        if (TAN) dout[i] = accT[nt][4 * j + i] * inv - o[i] * mu_n;
+        if (TAN) dout[i] = __builtin_fmaf(-o[i], mu_n, accT[nt][4 * j + i] * inv);
       }
       *reinterpret_cast<uint2 *>(ob + d0) = make_uint2(pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3]));
       if (TAN)

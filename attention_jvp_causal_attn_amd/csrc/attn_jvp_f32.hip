@@ -26,20 +26,13 @@ constexpr int TPR = 4;          // lanes per row
 static_assert(BM * TPR == kThreads, "one row per 4 lanes");
 constexpr float kNegInf = -__builtin_inff();
 
-__device__ __forceinline__ int xcd_logical(int w, int G) {
-  const int xcd = w & 7, local = w >> 3;
-  const int q = G >> 3, r = G & 7;
-  return xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
-}
-
 template <int D, bool TAN>
 __global__ __launch_bounds__(kThreads) void attn_jvp_f32_kernel(KernelParams p) {
   constexpr int DS = D / TPR;   // dims per lane
   constexpr int LD = D + 4;     // padded LDS row (floats)
   __shared__ float Ks[BN * LD], dKs[BN * LD], Vs[BN * LD], dVs[BN * LD];
 
-  const int G = p.n_tiles * p.B * p.H;
-  const int L = xcd_logical(int(blockIdx.x), G);
+  const int L = work_item(int(blockIdx.x), p);
   const int slot = L % p.n_tiles;
   const int bh = L / p.n_tiles;
   const int head = bh % p.H, batch = bh / p.H;
@@ -129,7 +122,7 @@ __global__ __launch_bounds__(kThreads) void attn_jvp_f32_kernel(KernelParams p) 
     for (int j = 0; j < BN; ++j) {
       s[j] = expf(s[j] - m_use);  // now the weight p_j
       lsum += s[j];
-      if (TAN) musum += s[j] * ds[j];
+      if (TAN) musum = __builtin_fmaf(s[j], ds[j], musum);
     }
     l_run = l_run * alpha + lsum;
     if (TAN) mu_run = mu_run * alpha + musum;
@@ -159,7 +152,7 @@ __global__ __launch_bounds__(kThreads) void attn_jvp_f32_kernel(KernelParams p) 
   for (int x = 0; x < DS; ++x) {
     const float ov = acc[x] * inv;
     o[x] = ov;
-    if (TAN) dout[x] = tac[x] * inv - ov * mu_n;
+    if (TAN) dout[x] = __builtin_fmaf(-ov, mu_n, tac[x] * inv);
   }
 }
 

@@ -57,7 +57,29 @@ struct KernelParams {
   const uint32_t *partial_bits;  // n_partial blocks, then one all-ones block
   int32_t n_tiles;
   int32_t n_partial;
+  // Workgroup -> (slice, tile slot) map, see work_item().  map_group = 0:
+  // identity; else XCDs form groups of map_group, each group owning
+  // map_slices consecutive (batch, head) slices, member XCD u of a group
+  // taking tile slots u, u + map_group, ... (map_slots of them) of each.
+  int32_t map_group;
+  int32_t map_slices;
+  int32_t map_slots;
 };
+
+#if defined(__HIP__)
+// Workgroup w is dispatched to XCD w % 8 (its position in that XCD's stream
+// is w / 8).  Returns the work item (slice * n_tiles + slot) of w: each XCD
+// receives an equal share of work (interleaved heavy-first slots) and the
+// workgroups resident on one XCD at a time belong to the same slice, so they
+// stream the same key blocks through that XCD's L2.
+__device__ __forceinline__ int work_item(int w, const KernelParams &p) {
+  if (p.map_group == 0) return w;
+  const int x = w & 7, local = w >> 3;
+  const int grp = x / p.map_group, mem = x % p.map_group;
+  const int sl = local / p.map_slots, k = local % p.map_slots;
+  return (grp * p.map_slices + sl) * p.n_tiles + mem + k * p.map_group;
+}
+#endif
 
 }  // namespace attnjvp
 

@@ -284,6 +284,39 @@ def test_outputs_fully_written_and_in_bounds(dtype):
         assert torch.isfinite(buf[G:-G]).all()
 
 
+# (B, H, n): the B*H slices and n / 128 query tiles select each branch of the
+# workgroup -> work map: XCD groups of 8, 4, 2 and 1 slices' worth, and the
+# identity map when the tiles do not split evenly over a group.
+WORK_MAP_CASES = [
+    (1, 3, 1024),  # 3 slices, 8 tiles: one group of 8 XCDs, 1 tile slot in 8 each
+    (1, 2, 512),   # groups of 4 XCDs
+    (2, 3, 256),   # 6 slices: groups of 4 XCDs, 2 tiles -> identity map
+    (1, 4, 300),   # groups of 2 XCDs, 3 tiles -> identity map
+    (2, 5, 512),   # 10 slices: groups of 4 XCDs, 5 slices per group
+    (1, 2, 1024),  # groups of 4 XCDs, 2 tile slots each
+    (4, 2, 200),   # 8 slices: one slice group per XCD
+]
+
+
+@pytest.mark.parametrize("B,H,n", WORK_MAP_CASES)
+def test_every_tile_of_every_slice_computed_once(B, H, n):
+    say(f"case: dense bf16 B={B} H={H} n={n} (work map)")
+    pred = dense_allowed(n, n)
+    x = make_random(B, n, H, 64, dtype="bf16", seed=9100 + 10 * B + H, tangent_std=0.1)
+    xd = to_dev(x)
+    o = torch.full_like(xd["q"], float("nan"))
+    do = torch.full_like(xd["q"], float("nan"))
+    lse = torch.full((B, H, n), float("nan"), dtype=torch.float32, device=DEV)
+    aj.attn_jvp_fwd(xd["q"], xd["k"], xd["v"], xd["dq"], xd["dk"], xd["dv"],
+                    aj.attn_jvp_mask_dense(n, n), o=o, d_o=do, lse=lse)
+    torch.cuda.synchronize()
+    O, dO, LSE = masked_attention_jvp(x["q"], x["k"], x["v"], x["dq"], x["dk"], x["dv"], pred)
+    tol = TOL[torch.bfloat16]
+    check("O", f64(o), O, tol)
+    check("dO", f64(do), dO, tol)
+    check("LSE", f64(lse), LSE, tol)
+
+
 def test_strided_views_of_fused_buffers():
     # Q/dQ/O/dO and K/V/dK/dV as views of fused [B, N, 3, H, D]-style buffers
     pred = tf_allowed(4, 45, 1)
