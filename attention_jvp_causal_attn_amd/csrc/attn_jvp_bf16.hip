@@ -1,4 +1,6 @@
-// Fused primal + tangent masked attention for gfx950 (bf16 in, fp32 accumulate).
+// Fused primal + tangent masked attention for gfx950, head dim 64 (bf16 in,
+// fp32 accumulate); head dim 128 runs the eight-wave kernel of
+// attn_jvp_bf16_wide.hip.
 //
 // One online-softmax pass computes O, LSE and dO ("Causal-rCM ..." summary,
 // Appendix B: the tangent rides the primal FlashAttention pass with shared
@@ -120,6 +122,7 @@ __device__ __forceinline__ float xor32(float v) { return __shfl_xor(v, 32, 64); 
 // Tracked by vmcnt; the kernel waits for it explicitly before the barrier that
 // publishes a stage.
 __device__ __forceinline__ void dma16(const void *base, uint32_t voff, uint32_t lds_wave) {
+  lds_wave = __builtin_amdgcn_readfirstlane(lds_wave);  // wave-uniform: keep it scalar
   // one wait state between the M0 write and the LDS-DMA that reads it
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :
@@ -505,7 +508,7 @@ hipError_t launch(const KernelParams &p, hipStream_t stream) {
 
 int launch_bf16(const KernelParams &p, int D, bool tangent, void *stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (D == 128) return tangent ? launch<128, true>(p, s) : launch<128, false>(p, s);
+  if (D == 128) return launch_bf16_wide(p, tangent, stream);
   if (D == 64) return tangent ? launch<64, true>(p, s) : launch<64, false>(p, s);
   return hipErrorInvalidValue;
 }

@@ -1,0 +1,440 @@
+// Fused primal + tangent masked attention for gfx950, head dim 128
+// (bf16 in, fp32 accumulate).
+//
+// One online-softmax pass computes O, LSE and dO ("Causal-rCM ..." summary,
+// Appendix B: the tangent rides the primal FlashAttention pass with shared
+// rescaling, masked pairs carry no tangent, one sparse schedule of admissible
+// key blocks serves the primal and the tangent scores).  Per query row the
+// pass keeps a reference max m, the sum l of exp(s - m), the sum mu of
+// exp(s - m) * ds, and two D-wide accumulators
+//     A = sum exp(s - m) v,   T = sum exp(s - m) (ds v + dv),
+// all rescaled by the same factor exp(m_old - m_new) when m moves, and ends
+// with O = A / l, dO = T / l - O * (mu / l), LSE = m + ln l.
+//
+// Work decomposition (MI355X-first):
+//  * one workgroup = 8 waves = 256 query rows of one (batch, head), two waves
+//    per SIMD: while one wave of a SIMD runs its vector-ALU softmax, scalar
+//    and LDS work, the other keeps the matrix core busy (one wave alone
+//    cannot: an MFMA holds its own wave's issue for about half its run time);
+//  * each wave owns 32 rows, one lane per row in each half-wave, so the
+//    per-row softmax state lives in a lane and only the two half-waves
+//    exchange the row max (and only when it moves);
+//  * scores are computed transposed, S^T = K Q^T and dS^T = K dQ^T + dK Q^T,
+//    with v_mfma_f32_32x32x16_bf16: K / dK from LDS as the A operand, Q in
+//    registers and dQ in LDS (staged once per tile) as the B operand;
+//  * the accumulators are transposed too, A^T += V^T P^T and
+//    T^T += V^T (P*dS)^T + dV^T P^T, so the MFMA output of the score step is
+//    already the B operand of the value step (no shuffle of P); K rows are
+//    read in a permuted order (bits 2 and 3 of the row swapped) so that each
+//    lane's 8 probabilities of a 16-key step are 8 consecutive keys;
+//  * V and dV stay row-major in LDS; the transposed V^T operand comes from
+//    ds_read_b64_tr_b16 (each group of 16 lanes turns 4 keys x 16 dims into
+//    16 lanes x 4 keys);
+//  * key blocks of 32 rows of K, dK, V, dV (and the admissible-key bits of
+//    the block) go HBM -> LDS with direct-to-LDS loads, one 16-byte chunk per
+//    lane per tensor, into a 2-stage ring: block j + 1 is copied while block
+//    j is computed; tiles are XOR-swizzled in 16-byte chunks so the operand
+//    reads hit distinct banks;
+//  * every value lives in the 256 VGPRs a wave has at two waves per SIMD
+//    (accumulators included, so the rare rescale is plain vector code); the
+//    reference max moves only when a row max exceeds it by more than 2^8, so
+//    p = exp2(s - m) stays below 2^8, far inside fp32 and bf16 range;
+//  * workgroups are mapped to work so that each XCD receives an equal share
+//    of every group of (batch, head) slices, as interleaved heavy-first tile
+//    slots, while the workgroups resident on one XCD at a time belong to the
+//    same slice and stream the same key blocks through that XCD's L2
+//    (work_item).
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+
+#include "internal.h"
+
+namespace attnjvp {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int D = 128;
+constexpr int kThreads = 512;
+constexpr int kWaves = 8;
+constexpr int BM = kBf16BlockMWide;  // 256 query rows per workgroup
+constexpr int BN = kBf16BlockN;      // 32 keys per block
+constexpr int kStages = 2;
+constexpr int KCH = D / 8;           // 16-byte chunks per row
+constexpr int KSTEPS = D / 16;
+constexpr int DT = D / 32;
+static_assert(BM == 32 * kWaves && BN == 32, "one wave per 32 rows, 32-key blocks");
+
+constexpr float kNegInf = -__builtin_inff();
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kRescaleSlack = 8.0f;  // log2 units: p <= 2^8 between rescales
+constexpr int kEntChunk = 512;        // schedule entries staged in LDS at a time
+
+struct alignas(16) StageTile {
+  uint4 k[BN * KCH];
+  uint4 dk[BN * KCH];
+  uint4 v[BN * KCH];
+  uint4 dv[BN * KCH];
+  uint32_t bits[BM];
+};
+
+// Position of K row m of the 32x32 score tile: bits 2 and 3 swapped.  The
+// MFMA output element (row 8j + 4h + i) then holds key 16(j/2) + 8h + 4(j%2) + i,
+// so lane-half h owns keys 16s + 8h + 0..7 of value step s, in register order.
+__device__ __forceinline__ int swap_bits23(int m) {
+  return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
+}
+// 16-byte-chunk XOR swizzles: row-operand reads (K, dK, dQ) touch 16 rows at
+// one chunk; transposed reads (V, dV) touch 4 rows x 4 chunks.
+__device__ __forceinline__ int k_swz(int row) { return row & 15; }
+__device__ __forceinline__ int v_swz(int row) { return 4 * (row & 3); }
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 x) { return __builtin_bit_cast(bf16x8, x); }
+
+// Round to nearest even, two values per v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+__device__ __forceinline__ bf16x8 to_bf16x8(const float *x) {
+  const f32x8 v = {x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]};
+  return __builtin_convertvector(v, bf16x8);
+}
+__device__ __forceinline__ float xor32(float v) { return __shfl_xor(v, 32, 64); }
+
+// 16 bytes per lane from global memory (wave-uniform base + per-lane byte
+// offset) straight into LDS at lds_wave + 16 * lane (lds_wave wave-uniform).
+// Tracked by vmcnt; the kernel waits for it explicitly before the barrier that
+// publishes a stage.  One wait state separates the M0 write from the copy.
+__device__ __forceinline__ void dma16(const void *base, uint32_t voff, uint32_t lds_wave) {
+  lds_wave = __builtin_amdgcn_readfirstlane(lds_wave);  // wave-uniform: keep it scalar
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(base), "s"(lds_wave)
+               : "memory", "m0");
+}
+// s_waitcnt vmcnt(N), other counters untouched (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// One 16-byte chunk per lane per tensor: 512 lanes cover a 32 x 128 tile.
+static_assert(BN * KCH == kThreads, "one chunk per lane per tensor tile");
+
+// Per-lane byte offsets inside a key block (K-swizzled, V-swizzled).
+struct DmaOffsets {
+  uint32_t k, v;
+};
+__device__ __forceinline__ DmaOffsets dma_offsets(int64_t k_sn, int rows_valid) {
+  const int q = threadIdx.x;
+  const int row = q / KCH, pch = q % KCH;
+  const uint32_t roff = uint32_t(min(row, rows_valid - 1)) * uint32_t(k_sn) * 2u;
+  return {roff + uint32_t(pch ^ k_swz(row)) * 16u, roff + uint32_t(pch ^ v_swz(row)) * 16u};
+}
+
+// Issue the direct-to-LDS copies of the key block starting at key key0 into
+// the stage tile at LDS byte address st.
+template <bool TAN>
+__device__ __forceinline__ void issue_block(uint32_t st, int wave, const KernelParams &p,
+                                            const __bf16 *kb_, const __bf16 *dkb_,
+                                            const __bf16 *vb_, const __bf16 *dvb_, int key0,
+                                            const uint32_t *bits_src) {
+  const int lane = threadIdx.x & 63;
+  const int64_t boff = int64_t(key0) * p.k_sn;
+  // rebuilt per block (cheaper than holding them in registers); rows past n_k
+  // re-read the last key, masked out by the schedule
+  const DmaOffsets o = dma_offsets(p.k_sn, min(BN, p.n_k - key0));
+  const uint32_t chunk = uint32_t(wave * 64) * 16u;
+  dma16(kb_ + boff, o.k, st + uint32_t(offsetof(StageTile, k)) + chunk);
+  dma16(vb_ + boff, o.v, st + uint32_t(offsetof(StageTile, v)) + chunk);
+  if (TAN) {
+    dma16(dkb_ + boff, o.k, st + uint32_t(offsetof(StageTile, dk)) + chunk);
+    dma16(dvb_ + boff, o.v, st + uint32_t(offsetof(StageTile, dv)) + chunk);
+  }
+  // mask bits: BM words = 64 chunks; wave w copies chunks 8w .. 8w+7 (lanes 0..7)
+  if (lane < 8)
+    dma16(bits_src, uint32_t(wave * 8 + lane) * 16u,
+          st + uint32_t(offsetof(StageTile, bits)) + uint32_t(wave) * 128u);
+}
+
+// S^T = K Q^T and dS^T = K dQ^T + dK Q^T; Q from registers, dQ from LDS.
+template <bool TAN>
+__device__ __forceinline__ void score_block(const StageTile *st, const uint4 *dq_lds,
+                                            const bf16x8 *qf, int row_in_tile, f32x16 &S,
+                                            f32x16 &dS) {
+  const int lane = threadIdx.x & 63;
+  const int col = lane & 31, hh = lane >> 5;
+  const int krow = swap_bits23(col);
+  const uint4 *Ks = st->k + krow * KCH;
+  const uint4 *dKs = st->dk + krow * KCH;
+  const uint4 *dQs = dq_lds + row_in_tile * KCH;
+  // opaque per call: the per-step addresses are rebuilt each block instead of
+  // being held in registers across the key loop
+  int kx = k_swz(krow), qx = k_swz(row_in_tile);
+  asm volatile("" : "+v"(kx), "+v"(qx));
+  S = f32x16{};
+  dS = f32x16{};
+#pragma unroll
+  for (int t = 0; t < KSTEPS; ++t) {
+    const bf16x8 kf = as_bf16x8(Ks[(2 * t + hh) ^ kx]);
+    S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[t], S, 0, 0, 0);
+    if (TAN) {
+      const bf16x8 dkf = as_bf16x8(dKs[(2 * t + hh) ^ kx]);
+      const bf16x8 dqf = as_bf16x8(dQs[(2 * t + hh) ^ qx]);
+      dS = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, dqf, dS, 0, 0, 0);
+      dS = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dkf, qf[t], dS, 0, 0, 0);
+    }
+    if (t % 2 == 1) __builtin_amdgcn_sched_barrier(0);  // bound the operand prefetch
+  }
+}
+
+// Masking, online-softmax update and value step of one key block.
+template <bool TAN>
+__device__ __forceinline__ void softmax_value_block(const StageTile *st, f32x16 S, f32x16 dS,
+                                                    f32x16 *accO, f32x16 *accT, float &m_ref,
+                                                    float &l_run, float &mu_run, bool partial,
+                                                    int row_in_tile, float scale_log2,
+                                                    float scale) {
+  const int lane = threadIdx.x & 63;
+  const int hh = lane >> 5;
+  if (partial) {
+    // this lane-half's keys 8hh + {0..7, 16..23}, so the bit positions below
+    // are constants
+    const uint32_t bits = st->bits[row_in_tile] >> (8 * hh);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int j = r >> 2, i = r & 3;
+      const int key = 16 * (j >> 1) + 4 * (j & 1) + i;
+      const bool ok = (bits >> key) & 1u;
+      S[r] = ok ? S[r] : kNegInf;
+      if (TAN) dS[r] = ok ? dS[r] : 0.f;
+    }
+  }
+  float mh = S[0];
+#pragma unroll
+  for (int r = 1; r < 16; ++r) mh = fmaxf(mh, S[r]);
+  mh *= scale_log2;
+  if (__builtin_amdgcn_ballot_w64(mh > m_ref + kRescaleSlack) != 0) {
+    const float mx = fmaxf(mh, xor32(mh));
+    const bool grow = mx > m_ref + kRescaleSlack;
+    const float m_new = grow ? mx : m_ref;
+    const float alpha = grow ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.f;
+    l_run *= alpha;
+    mu_run *= alpha;
+#pragma unroll
+    for (int nt = 0; nt < DT; ++nt) {
+      accO[nt] *= alpha;
+      if (TAN) accT[nt] *= alpha;
+    }
+    m_ref = m_new;
+  }
+  const float m_use = m_ref == kNegInf ? 0.f : m_ref;
+  float pr[16], pds[16];
+  float lsum = 0.f, musum = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], scale_log2, -m_use));
+    lsum += pr[r];
+    if (TAN) {
+      const float dss = dS[r] * scale;
+      pds[r] = pr[r] * dss;
+      musum = __builtin_fmaf(pr[r], dss, musum);
+    }
+  }
+  l_run += lsum;
+  if (TAN) mu_run += musum;
+  bf16x8 pb[2], pdsb[2];
+  pb[0] = to_bf16x8(pr);
+  pb[1] = to_bf16x8(pr + 8);
+  if (TAN) {
+    pdsb[0] = to_bf16x8(pds);
+    pdsb[1] = to_bf16x8(pds + 8);
+  }
+  const int g = lane >> 4, jl = lane & 15;
+  int dcol = 16 * (g & 1) + 4 * (jl & 3);
+  int krel = 8 * hh + (jl >> 2);
+  asm volatile("" : "+v"(dcol), "+v"(krel));
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+#pragma unroll
+    for (int nt = 0; nt < DT; ++nt) {
+      const int d = 32 * nt + dcol;
+      bf16x4 vh[2], dvh[2];
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int key = 16 * s + 4 * half + krel;
+        const int chunk = key * KCH + ((d >> 3) ^ v_swz(key));
+        const char *vp = reinterpret_cast<const char *>(st->v + chunk) + (d & 7) * 2;
+        vh[half] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (__attribute__((address_space(3))) bf16x4 *)(vp));
+        if (TAN) {
+          const char *dvp = reinterpret_cast<const char *>(st->dv + chunk) + (d & 7) * 2;
+          dvh[half] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (__attribute__((address_space(3))) bf16x4 *)(dvp));
+        }
+      }
+      const bf16x8 vf = __builtin_shufflevector(vh[0], vh[1], 0, 1, 2, 3, 4, 5, 6, 7);
+      accO[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[s], accO[nt], 0, 0, 0);
+      if (TAN) {
+        const bf16x8 dvf = __builtin_shufflevector(dvh[0], dvh[1], 0, 1, 2, 3, 4, 5, 6, 7);
+        accT[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pdsb[s], accT[nt], 0, 0, 0);
+        accT[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dvf, pb[s], accT[nt], 0, 0, 0);
+      }
+      if (nt % 2 == 1) __builtin_amdgcn_sched_barrier(0);  // bound the operand prefetch
+    }
+  }
+}
+
+template <bool TAN>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_jvp_bf16_wide_kernel(KernelParams p) {
+  __shared__ StageTile ring[kStages];
+  __shared__ uint4 dq_lds[TAN ? BM * KCH : 1];
+  __shared__ int2 ents[2][kEntChunk];
+
+  const int L = work_item(int(blockIdx.x), p);
+  const int slot = L % p.n_tiles;
+  const int bh = L / p.n_tiles;
+  const int head = bh % p.H, batch = bh / p.H;
+  const int tile = p.tile_order[slot];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 31, hh = lane >> 5;
+  const int row_in_tile = wave * 32 + col;
+  const uint32_t ring_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&ring[0]));
+  auto stage_lds = [&](int s) { return ring_lds + uint32_t(s) * uint32_t(sizeof(StageTile)); };
+  const int qrow = tile * BM + row_in_tile;
+  const bool qvalid = qrow < p.n_q;
+
+  const int64_t koff = int64_t(batch) * p.k_sb + int64_t(head) * p.k_sh;
+  const __bf16 *kb_ = static_cast<const __bf16 *>(p.k) + koff;
+  const __bf16 *vb_ = static_cast<const __bf16 *>(p.v) + koff;
+  const __bf16 *dkb_ = TAN ? static_cast<const __bf16 *>(p.dk) + koff : nullptr;
+  const __bf16 *dvb_ = TAN ? static_cast<const __bf16 *>(p.dv) + koff : nullptr;
+  const int64_t qoff = int64_t(batch) * p.q_sb + int64_t(head) * p.q_sh;
+
+  const int e0 = p.tile_offsets[tile], e1 = p.tile_offsets[tile + 1];
+  const int n = e1 - e0;
+  auto load_entries = [&](int c) {
+    int2 *dst = ents[c & 1];
+    const int base = e0 + c * kEntChunk;
+#pragma unroll
+    for (int i = threadIdx.x; i < kEntChunk; i += kThreads)
+      dst[i] = base + i < e1 ? p.entries[base + i] : make_int2(0, -1);
+  };
+  auto entry = [&](int j) {
+    const int2 e = ents[(j / kEntChunk) & 1][j % kEntChunk];
+    return make_int2(__builtin_amdgcn_readfirstlane(e.x), __builtin_amdgcn_readfirstlane(e.y));
+  };
+  auto bits_of = [&](int2 ent) {
+    return p.partial_bits + int64_t(ent.y >= 0 ? ent.y : p.n_partial) * BM;
+  };
+
+  load_entries(0);
+  __syncthreads();
+  const int2 no_ent = make_int2(0, -1);
+  int2 ent_c = n > 0 ? entry(0) : no_ent;
+  int2 ent_1 = n > 1 ? entry(1) : no_ent;
+  if (n > 0)
+    issue_block<TAN>(stage_lds(0), wave, p, kb_, dkb_, vb_, dvb_, ent_c.x * BN, bits_of(ent_c));
+
+  // dQ tile -> LDS (rows past n_q re-read the last row), Q -> registers.
+  if (TAN) {
+    const uint32_t dq_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&dq_lds[0]));
+    const __bf16 *dqb = static_cast<const __bf16 *>(p.dq) + qoff;
+#pragma unroll
+    for (int i = 0; i < BM * KCH / kThreads; ++i) {
+      const int q = i * kThreads + threadIdx.x;
+      const int row = q / KCH, pch = q % KCH;
+      const int grow = min(tile * BM + row, p.n_q - 1);
+      const uint32_t off = uint32_t(grow) * uint32_t(p.q_sn) * 2u + uint32_t(pch ^ k_swz(row)) * 16u;
+      dma16(dqb, off, dq_base + uint32_t(i * kThreads + wave * 64) * 16u);
+    }
+  }
+  bf16x8 qf[KSTEPS];
+  {
+    const int qr = qvalid ? qrow : 0;
+    const __bf16 *qb = static_cast<const __bf16 *>(p.q) + qoff + int64_t(qr) * p.q_sn + 8 * hh;
+#pragma unroll
+    for (int t = 0; t < KSTEPS; ++t) qf[t] = as_bf16x8(*reinterpret_cast<const uint4 *>(qb + 16 * t));
+  }
+
+  f32x16 accO[DT], accT[DT];
+#pragma unroll
+  for (int nt = 0; nt < DT; ++nt) {
+    accO[nt] = f32x16{};
+    accT[nt] = f32x16{};
+  }
+  float m_ref = kNegInf, l_run = 0.f, mu_run = 0.f;
+
+  for (int j = 0; j < n; ++j) {
+    if ((j + 2) % kEntChunk == 0 && j + 2 < n) load_entries((j + 2) / kEntChunk);
+    wait_vmcnt<0>();  // block j (and, first time, dQ and Q) has landed
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    const StageTile *st = &ring[j & 1];
+    f32x16 S, dS;
+    score_block<TAN>(st, dq_lds, qf, row_in_tile, S, dS);
+    // block j + 1 into the other stage (released by the barrier)
+    if (j + 1 < n)
+      issue_block<TAN>(stage_lds((j + 1) & 1), wave, p, kb_, dkb_, vb_, dvb_, ent_1.x * BN,
+                       bits_of(ent_1));
+    softmax_value_block<TAN>(st, S, dS, accO, accT, m_ref, l_run, mu_run, ent_c.y >= 0,
+                             row_in_tile, p.scale_log2, p.scale);
+    ent_c = ent_1;
+    ent_1 = j + 2 < n ? entry(j + 2) : no_ent;
+  }
+
+  const float l_tot = l_run + xor32(l_run);
+  const float mu_tot = TAN ? mu_run + xor32(mu_run) : 0.f;
+  if (!qvalid) return;
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const float mu_n = mu_tot * inv;
+  if (hh == 0) {
+    p.lse[(int64_t(batch) * p.H + head) * p.n_q + qrow] =
+        l_tot > 0.f ? (m_ref + __log2f(l_tot)) * kLn2 : kNegInf;
+  }
+  const int64_t ooff = qoff + int64_t(qrow) * p.q_sn;
+  __bf16 *ob = static_cast<__bf16 *>(p.o) + ooff;
+  __bf16 *dob = TAN ? static_cast<__bf16 *>(p.d_o) + ooff : nullptr;
+#pragma unroll
+  for (int nt = 0; nt < DT; ++nt) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int d0 = 32 * nt + 8 * j + 4 * hh;
+      float o[4], dout[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        o[i] = accO[nt][4 * j + i] * inv;
+        if (TAN) dout[i] = __builtin_fmaf(-o[i], mu_n, accT[nt][4 * j + i] * inv);
+      }
+      *reinterpret_cast<uint2 *>(ob + d0) = make_uint2(pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3]));
+      if (TAN)
+        *reinterpret_cast<uint2 *>(dob + d0) =
+            make_uint2(pack_bf16(dout[0], dout[1]), pack_bf16(dout[2], dout[3]));
+    }
+  }
+}
+
+}  // namespace
+
+int launch_bf16_wide(const KernelParams &p, bool tangent, void *stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t G = int64_t(p.n_tiles) * p.B * p.H;
+  if (tangent)
+    hipLaunchKernelGGL(attn_jvp_bf16_wide_kernel<true>, dim3(unsigned(G)), dim3(kThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL(attn_jvp_bf16_wide_kernel<false>, dim3(unsigned(G)), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace attnjvp

@@ -24,7 +24,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_F32_VALU_TFLOPS = 157.3
 # sources that decide what the bf16 JVP launch does (kernel, launch map, params)
-KERNEL_SOURCES = ["attention_jvp_causal_attn_amd/csrc/attn_jvp_bf16.hip",
+KERNEL_SOURCES = ["attention_jvp_causal_attn_amd/csrc/attn_jvp_bf16_wide.hip",
                   "attention_jvp_causal_attn_amd/csrc/internal.h",
                   "attention_jvp_causal_attn_amd/csrc/attn_jvp_api.cpp"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_jvp_bf16_chunkwise65k_traffic.md")

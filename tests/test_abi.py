@@ -35,7 +35,8 @@ def test_version_and_status_strings():
     for st in range(-8, 1):
         assert aj.attn_jvp_status_str(st) not in ("", "unknown status")
     assert aj.attn_jvp_status_str(-99) == "unknown status"
-    assert aj.attn_jvp_tile_shape(aj.ATTN_JVP_BF16, 128) == (128, 32)
+    assert aj.attn_jvp_tile_shape(aj.ATTN_JVP_BF16, 128) == (256, 32)
+    assert aj.attn_jvp_tile_shape(aj.ATTN_JVP_BF16, 64) == (128, 32)
     assert aj.attn_jvp_tile_shape(aj.ATTN_JVP_F32, 64) == (64, 32)
     with pytest.raises(aj.AttnJvpError):
         aj.attn_jvp_tile_shape(aj.ATTN_JVP_BF16, 96)

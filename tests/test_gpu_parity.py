@@ -298,11 +298,21 @@ WORK_MAP_CASES = [
 ]
 
 
-@pytest.mark.parametrize("B,H,n", WORK_MAP_CASES)
-def test_every_tile_of_every_slice_computed_once(B, H, n):
-    say(f"case: dense bf16 B={B} H={H} n={n} (work map)")
+# The same branches for head dim 128 (256-row tiles).
+WORK_MAP_CASES_128 = [
+    (1, 3, 2048),  # one group of 8 XCDs
+    (1, 2, 1024),  # groups of 4 XCDs
+    (1, 4, 600),   # groups of 2 XCDs, 3 tiles -> identity map
+    (4, 2, 400),   # 8 slices: one slice group per XCD
+]
+
+
+@pytest.mark.parametrize("B,H,n,D", [c + (64,) for c in WORK_MAP_CASES] +
+                         [c + (128,) for c in WORK_MAP_CASES_128])
+def test_every_tile_of_every_slice_computed_once(B, H, n, D):
+    say(f"case: dense bf16 B={B} H={H} n={n} D={D} (work map)")
     pred = dense_allowed(n, n)
-    x = make_random(B, n, H, 64, dtype="bf16", seed=9100 + 10 * B + H, tangent_std=0.1)
+    x = make_random(B, n, H, D, dtype="bf16", seed=9100 + 10 * B + H + D, tangent_std=0.1)
     xd = to_dev(x)
     o = torch.full_like(xd["q"], float("nan"))
     do = torch.full_like(xd["q"], float("nan"))
