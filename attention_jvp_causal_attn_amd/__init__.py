@@ -188,8 +188,6 @@ def attn_jvp_fwd(q, k, v, dq, dk, dv, mask, scale=None, o=None, d_o=None, lse=No
     """
     import torch
     tangent = dq is not None or dk is not None or dv is not None
-    if tangent and (dq is None or dk is None or dv is None):
-        raise ValueError("pass all of dq, dk, dv or none of them")
     if q.dim() != 4 or k.dim() != 4:
         raise ValueError("tensors must be [B, N, H, D]")
     B, n_q, H, D = q.shape

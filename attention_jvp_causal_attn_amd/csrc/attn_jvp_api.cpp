@@ -131,9 +131,8 @@ extern "C" int attn_jvp_fwd(const attn_jvp_args *a, const attn_jvp_mask *m, void
   if (!a || !m) return ATTN_JVP_ERR_NULL;
   if (a->dtype != ATTN_JVP_BF16 && a->dtype != ATTN_JVP_F32) return ATTN_JVP_ERR_DTYPE;
   if (!a->q || !a->k || !a->v || !a->o || !a->lse) return ATTN_JVP_ERR_NULL;
-  const int n_tan = (a->dq != nullptr) + (a->dk != nullptr) + (a->dv != nullptr);
-  if (n_tan != 0 && n_tan != 3) return ATTN_JVP_ERR_UNSUPPORTED;
-  const bool tangent = n_tan == 3;
+  // any tangent given: JVP, the absent ones zero; none: primal only
+  const bool tangent = a->dq != nullptr || a->dk != nullptr || a->dv != nullptr;
   if (tangent && !a->d_o) return ATTN_JVP_ERR_NULL;
   if (a->B <= 0 || a->H <= 0 || a->n_q <= 0 || a->n_k <= 0) return ATTN_JVP_ERR_SHAPE;
   if (a->D != 64 && a->D != 128) return ATTN_JVP_ERR_UNSUPPORTED;

@@ -137,6 +137,10 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// A zero row: the copy source of an absent (zero) tangent tensor, read with
+// row-independent offsets.
+__device__ __align__(16) uint4 kZeroRow[16];
+
 template <int D, bool TAN>
 struct Dma {
   static constexpr int KCH = D / 8;                 // 16-byte chunks per key row
@@ -184,14 +188,20 @@ __device__ __forceinline__ void issue_block(uint32_t st, int wave, const KernelP
   const int64_t boff = int64_t(key0) * p.k_sn;
   DmaOffsets<D, TAN> o = full_off;
   if (key0 + BN > p.n_k) dma_offsets<D, TAN>(o, p.k_sn, p.n_k - key0);  // last block only
+  // an absent tangent tensor is zero: copy the zero row into every row
+  DmaOffsets<D, TAN> oz;
+  if (TAN) dma_offsets<D, TAN>(oz, 0, 1);
+  const bool zk = dkb_ == nullptr, zv = dvb_ == nullptr;
 #pragma unroll
   for (int i = 0; i < M::PER_TENSOR; ++i) {
     const uint32_t chunk = uint32_t(i * kThreads + wave * 64) * 16u;  // this wave-instruction
     dma16(kb_ + boff, o.k[i], st + uint32_t(offsetof(T, k)) + chunk);
     dma16(vb_ + boff, o.v[i], st + uint32_t(offsetof(T, v)) + chunk);
     if (TAN) {
-      dma16(dkb_ + boff, o.k[i], st + uint32_t(offsetof(T, dk)) + chunk);
-      dma16(dvb_ + boff, o.v[i], st + uint32_t(offsetof(T, dv)) + chunk);
+      dma16(zk ? static_cast<const void *>(kZeroRow) : dkb_ + boff, zk ? oz.k[i] : o.k[i],
+            st + uint32_t(offsetof(T, dk)) + chunk);
+      dma16(zv ? static_cast<const void *>(kZeroRow) : dvb_ + boff, zv ? oz.v[i] : o.v[i],
+            st + uint32_t(offsetof(T, dv)) + chunk);
     }
   }
   // mask bits: BM words = 32 chunks; wave w copies chunks 8w .. 8w+7 (lanes 0..7)
@@ -375,8 +385,9 @@ void attn_jvp_bf16_kernel(KernelParams p) {
   const int64_t koff = int64_t(batch) * p.k_sb + int64_t(head) * p.k_sh;
   const __bf16 *kb_ = static_cast<const __bf16 *>(p.k) + koff;
   const __bf16 *vb_ = static_cast<const __bf16 *>(p.v) + koff;
-  const __bf16 *dkb_ = TAN ? static_cast<const __bf16 *>(p.dk) + koff : nullptr;
-  const __bf16 *dvb_ = TAN ? static_cast<const __bf16 *>(p.dv) + koff : nullptr;
+  // absent tangent tensors (NULL) are zero
+  const __bf16 *dkb_ = TAN && p.dk ? static_cast<const __bf16 *>(p.dk) + koff : nullptr;
+  const __bf16 *dvb_ = TAN && p.dv ? static_cast<const __bf16 *>(p.dv) + koff : nullptr;
 
   const int e0 = p.tile_offsets[tile], e1 = p.tile_offsets[tile + 1];
   const int n = e1 - e0;
@@ -419,11 +430,11 @@ void attn_jvp_bf16_kernel(KernelParams p) {
     const int qr = qvalid ? qrow : 0;
     const int64_t off = int64_t(batch) * p.q_sb + int64_t(head) * p.q_sh + int64_t(qr) * p.q_sn + 8 * hh;
     const __bf16 *qb = static_cast<const __bf16 *>(p.q) + off;
-    const __bf16 *dqb = TAN ? static_cast<const __bf16 *>(p.dq) + off : nullptr;
+    const __bf16 *dqb = TAN && p.dq ? static_cast<const __bf16 *>(p.dq) + off : nullptr;
 #pragma unroll
     for (int t = 0; t < KSTEPS; ++t) {
       qf[t] = as_bf16x8(*reinterpret_cast<const uint4 *>(qb + 16 * t));
-      if (TAN) dqf[t] = as_bf16x8(*reinterpret_cast<const uint4 *>(dqb + 16 * t));
+      if (TAN) dqf[t] = dqb ? as_bf16x8(*reinterpret_cast<const uint4 *>(dqb + 16 * t)) : bf16x8{};
     }
   }
   // Q, dQ and the first block are in before the loop: the loop itself then

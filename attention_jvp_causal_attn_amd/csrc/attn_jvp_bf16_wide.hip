@@ -126,6 +126,10 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// A zero row: the copy source of an absent (zero) tangent tensor, read with
+// row-independent offsets.
+__device__ __align__(16) uint4 kZeroRow[KCH];
+
 // One 16-byte chunk per lane per tensor: 512 lanes cover a 32 x 128 tile.
 static_assert(BN * KCH == kThreads, "one chunk per lane per tensor tile");
 
@@ -156,8 +160,13 @@ __device__ __forceinline__ void issue_block(uint32_t st, int wave, const KernelP
   dma16(kb_ + boff, o.k, st + uint32_t(offsetof(StageTile, k)) + chunk);
   dma16(vb_ + boff, o.v, st + uint32_t(offsetof(StageTile, v)) + chunk);
   if (TAN) {
-    dma16(dkb_ + boff, o.k, st + uint32_t(offsetof(StageTile, dk)) + chunk);
-    dma16(dvb_ + boff, o.v, st + uint32_t(offsetof(StageTile, dv)) + chunk);
+    // an absent tangent tensor is zero: copy the zero row into every row
+    const DmaOffsets oz = dma_offsets(0, 1);
+    const bool zk = dkb_ == nullptr, zv = dvb_ == nullptr;
+    dma16(zk ? static_cast<const void *>(kZeroRow) : dkb_ + boff, zk ? oz.k : o.k,
+          st + uint32_t(offsetof(StageTile, dk)) + chunk);
+    dma16(zv ? static_cast<const void *>(kZeroRow) : dvb_ + boff, zv ? oz.v : o.v,
+          st + uint32_t(offsetof(StageTile, dv)) + chunk);
   }
   // mask bits: BM words = 64 chunks; wave w copies chunks 8w .. 8w+7 (lanes 0..7)
   if (lane < 8)
@@ -318,8 +327,9 @@ void attn_jvp_bf16_wide_kernel(KernelParams p) {
   const int64_t koff = int64_t(batch) * p.k_sb + int64_t(head) * p.k_sh;
   const __bf16 *kb_ = static_cast<const __bf16 *>(p.k) + koff;
   const __bf16 *vb_ = static_cast<const __bf16 *>(p.v) + koff;
-  const __bf16 *dkb_ = TAN ? static_cast<const __bf16 *>(p.dk) + koff : nullptr;
-  const __bf16 *dvb_ = TAN ? static_cast<const __bf16 *>(p.dv) + koff : nullptr;
+  // absent tangent tensors (NULL) are zero
+  const __bf16 *dkb_ = TAN && p.dk ? static_cast<const __bf16 *>(p.dk) + koff : nullptr;
+  const __bf16 *dvb_ = TAN && p.dv ? static_cast<const __bf16 *>(p.dv) + koff : nullptr;
   const int64_t qoff = int64_t(batch) * p.q_sb + int64_t(head) * p.q_sh;
 
   const int e0 = p.tile_offsets[tile], e1 = p.tile_offsets[tile + 1];
@@ -350,14 +360,17 @@ void attn_jvp_bf16_wide_kernel(KernelParams p) {
   // dQ tile -> LDS (rows past n_q re-read the last row), Q -> registers.
   if (TAN) {
     const uint32_t dq_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&dq_lds[0]));
-    const __bf16 *dqb = static_cast<const __bf16 *>(p.dq) + qoff;
+    const bool zq = p.dq == nullptr;
+    const void *dqb = zq ? static_cast<const void *>(kZeroRow)
+                         : static_cast<const void *>(static_cast<const __bf16 *>(p.dq) + qoff);
 #pragma unroll
     for (int i = 0; i < BM * KCH / kThreads; ++i) {
       const int q = i * kThreads + threadIdx.x;
       const int row = q / KCH, pch = q % KCH;
       const int grow = min(tile * BM + row, p.n_q - 1);
-      const uint32_t off = uint32_t(grow) * uint32_t(p.q_sn) * 2u + uint32_t(pch ^ k_swz(row)) * 16u;
-      dma16(dqb, off, dq_base + uint32_t(i * kThreads + wave * 64) * 16u);
+      const uint32_t roff = zq ? 0u : uint32_t(grow) * uint32_t(p.q_sn) * 2u;
+      dma16(dqb, roff + uint32_t(pch ^ k_swz(row)) * 16u,
+            dq_base + uint32_t(i * kThreads + wave * 64) * 16u);
     }
   }
   bf16x8 qf[KSTEPS];

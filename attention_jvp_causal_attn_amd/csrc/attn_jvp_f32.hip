@@ -48,14 +48,15 @@ __global__ __launch_bounds__(kThreads) void attn_jvp_f32_kernel(KernelParams p) 
   const int64_t koff = int64_t(batch) * p.k_sb + int64_t(head) * p.k_sh;
   const float *kg = static_cast<const float *>(p.k) + koff;
   const float *vg = static_cast<const float *>(p.v) + koff;
-  const float *dkg = TAN ? static_cast<const float *>(p.dk) + koff : nullptr;
-  const float *dvg = TAN ? static_cast<const float *>(p.dv) + koff : nullptr;
+  // absent tangent tensors (NULL) are zero
+  const float *dkg = TAN && p.dk ? static_cast<const float *>(p.dk) + koff : nullptr;
+  const float *dvg = TAN && p.dv ? static_cast<const float *>(p.dv) + koff : nullptr;
 
   float q[DS], dq[DS], acc[DS], tac[DS];
 #pragma unroll
   for (int e = 0; e < DS; ++e) {
     q[e] = qvalid ? static_cast<const float *>(p.q)[qoff + d0 + e] : 0.f;
-    dq[e] = (TAN && qvalid) ? static_cast<const float *>(p.dq)[qoff + d0 + e] : 0.f;
+    dq[e] = (TAN && qvalid && p.dq) ? static_cast<const float *>(p.dq)[qoff + d0 + e] : 0.f;
     acc[e] = 0.f;
     tac[e] = 0.f;
   }
@@ -75,10 +76,8 @@ __global__ __launch_bounds__(kThreads) void attn_jvp_f32_kernel(KernelParams p) 
         const int64_t off = int64_t(key) * p.k_sn + c;
         kk = *reinterpret_cast<const float4 *>(kg + off);
         vv = *reinterpret_cast<const float4 *>(vg + off);
-        if (TAN) {
-          dkk = *reinterpret_cast<const float4 *>(dkg + off);
-          dvv = *reinterpret_cast<const float4 *>(dvg + off);
-        }
+        if (TAN && dkg) dkk = *reinterpret_cast<const float4 *>(dkg + off);
+        if (TAN && dvg) dvv = *reinterpret_cast<const float4 *>(dvg + off);
       }
       *reinterpret_cast<float4 *>(&Ks[r * LD + c]) = kk;
       *reinterpret_cast<float4 *>(&Vs[r * LD + c]) = vv;

@@ -49,7 +49,7 @@ enum attn_jvp_status {
   ATTN_JVP_ERR_MASK = -5,        /* malformed mask description, or mask size
                                     differs from the tensors */
   ATTN_JVP_ERR_UNSUPPORTED = -6, /* valid but not implemented (head dim,
-                                    partly-NULL tangents, aliasing outputs) */
+                                    aliasing outputs) */
   ATTN_JVP_ERR_HIP = -7,         /* no usable HIP device, or a HIP call failed */
   ATTN_JVP_ERR_OOM = -8          /* host or device allocation failed */
 };
@@ -148,8 +148,9 @@ typedef struct attn_jvp_args {
   int32_t n_q, n_k;    /* query rows, key rows: must equal the mask's */
   int32_t D;           /* head dim: 64 or 128 */
   const void *q, *k, *v;
-  const void *dq, *dk, *dv; /* all non-NULL: JVP; all NULL: primal only (d_o
-                               untouched); mixed: ERR_UNSUPPORTED */
+  const void *dq, *dk, *dv; /* tangents; any of them NULL: that tangent is zero
+                               (e.g. dK = dV = 0 for detached cached keys);
+                               all NULL: primal only (d_o untouched) */
   void *o, *d_o;            /* outputs; must not alias any input */
   float *lse;               /* output, required */
   int64_t q_stride_b, q_stride_n, q_stride_h;

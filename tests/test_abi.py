@@ -75,8 +75,8 @@ BAD = [
     (dict(o=None), _lib.ATTN_JVP_ERR_NULL),
     (dict(lse=None), _lib.ATTN_JVP_ERR_NULL),
     (dict(d_o=None), _lib.ATTN_JVP_ERR_NULL),
-    (dict(dk=None), _lib.ATTN_JVP_ERR_UNSUPPORTED),
-    (dict(dq=None, dv=None), _lib.ATTN_JVP_ERR_UNSUPPORTED),
+    (dict(dk=None, d_o=None), _lib.ATTN_JVP_ERR_NULL),   # any tangent given needs d_o
+    (dict(dq=None, dv=None, d_o=None), _lib.ATTN_JVP_ERR_NULL),
     (dict(D=96), _lib.ATTN_JVP_ERR_UNSUPPORTED),
     (dict(B=0), _lib.ATTN_JVP_ERR_SHAPE),
     (dict(H=-1), _lib.ATTN_JVP_ERR_SHAPE),
@@ -116,6 +116,7 @@ def test_fwd_without_device_reports_hip_error():
     mask = aj.attn_jvp_mask_tf(4, 16, 1)
     assert _fwd(_args(mask), mask) == _lib.ATTN_JVP_ERR_HIP
     assert _fwd(_args(mask, dq=None, dk=None, dv=None, d_o=None), mask) == _lib.ATTN_JVP_ERR_HIP
+    assert _fwd(_args(mask, dk=None, dv=None), mask) == _lib.ATTN_JVP_ERR_HIP
 
 
 def test_python_binding_requires_gpu_tensors():

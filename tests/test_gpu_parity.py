@@ -327,6 +327,34 @@ def test_every_tile_of_every_slice_computed_once(B, H, n, D):
     check("LSE", f64(lse), LSE, tol)
 
 
+# Absent tangents are zero: a call with some of dq, dk, dv set to None equals,
+# bit for bit, the call with explicit zero tensors, and matches the oracle.
+TANGENT_SUBSETS = [("dq",), ("dk",), ("dv",), ("dk", "dv"), ("dq", "dk"), ("dq", "dv")]
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("bf16", 64), ("f32", 64)])
+@pytest.mark.parametrize("given", TANGENT_SUBSETS)
+def test_absent_tangents_are_zero(dtype, D, given):
+    say(f"case: {dtype} D={D} tangents given: {given}")
+    pred = tf_allowed(5, 37, 1)
+    x = make_random(1, pred.n_q, 2, D, dtype=dtype, seed=9300 + D + len(given), tangent_std=0.1)
+    for name in ("dq", "dk", "dv"):
+        if name not in given:
+            x[name] = torch.zeros_like(x[name])
+    xd = to_dev(x)
+    mask = aj.attn_jvp_mask_tf(5, 37, 1)
+    t = {name: (xd[name] if name in given else None) for name in ("dq", "dk", "dv")}
+    o1, do1, lse1 = aj.attn_jvp_fwd(xd["q"], xd["k"], xd["v"], t["dq"], t["dk"], t["dv"], mask)
+    o2, do2, lse2 = aj.attn_jvp_fwd(xd["q"], xd["k"], xd["v"], xd["dq"], xd["dk"], xd["dv"], mask)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(do1, do2) and torch.equal(lse1, lse2)
+    O, dO, LSE = masked_attention_jvp(x["q"], x["k"], x["v"], x["dq"], x["dk"], x["dv"], pred)
+    tol = TOL[torch.bfloat16 if dtype == "bf16" else torch.float32]
+    check("O", f64(o1), O, tol)
+    check("dO", f64(do1), dO, tol)
+    check("LSE", f64(lse1), LSE, tol)
+
+
 def test_strided_views_of_fused_buffers():
     # Q/dQ/O/dO and K/V/dK/dV as views of fused [B, N, 3, H, D]-style buffers
     pred = tf_allowed(4, 45, 1)
