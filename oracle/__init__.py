@@ -26,3 +26,4 @@ from .masks import (  # noqa: F401
     block_causal_allowed,
 )
 from .attn_jvp import masked_attention, masked_attention_jvp  # noqa: F401
+from .attn_bwd import masked_attention_grad  # noqa: F401
