@@ -106,6 +106,12 @@ def attn_jvp_mask_dense(n_q, n_k):
     return _new_mask(L.attn_jvp_mask_dense, int(n_q), int(n_k))
 
 
+def attn_jvp_mask_transpose(mask):
+    """The mask with key and query roles swapped (see attn_jvp.h)."""
+    L = _lib.lib()
+    return _new_mask(L.attn_jvp_mask_transpose, mask.handle)
+
+
 def attn_jvp_mask_info(mask):
     """dict(n_q, n_k, n_groups, n_ranges, n_visible_pairs)."""
     v = [ctypes.c_int32() for _ in range(4)]

@@ -51,6 +51,7 @@ SIGNATURES = {
     "attn_jvp_mask_export": (_i32, [_p, _pi32, _pi32, _pi32, _pi32]),
     "attn_jvp_mask_schedule": (_i32, [_p, _i32, _i32, _pi32, _pi64, _pi64, _pi32, _pi32,
                                       _pi32, _pi32, _pu32]),
+    "attn_jvp_mask_transpose": (_i32, [_p, _PPMASK]),
     "attn_jvp_mask_free": (None, [_p]),
     "attn_jvp_fwd": (_i32, [ctypes.POINTER(AttnJvpArgs), _p, _p]),
     "attn_jvp_tile_shape": (_i32, [_i32, _i32, _pi32, _pi32]),

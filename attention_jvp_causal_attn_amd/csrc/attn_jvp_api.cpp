@@ -80,8 +80,8 @@ int device_schedule_locked(const attn_jvp_mask *m, int device, int BM, int BN,
 
 }  // namespace
 
-extern "C" void attn_jvp_mask_free(attn_jvp_mask *m) {
-  if (!m) return;
+// Free the device schedules of a mask (and of its cached transpose).
+static void free_device_schedules(attn_jvp_mask *m) {
   int cur = -1;
   bool have_cur = hipGetDevice(&cur) == hipSuccess;
   for (auto &kv : m->dev_sched) {
@@ -89,6 +89,13 @@ extern "C" void attn_jvp_mask_free(attn_jvp_mask *m) {
     if (hipSetDevice(dev) == hipSuccess) (void)hipFree(kv.second.base);
   }
   if (have_cur && !m->dev_sched.empty()) (void)hipSetDevice(cur);
+  m->dev_sched.clear();
+  if (m->transposed) free_device_schedules(m->transposed.get());
+}
+
+extern "C" void attn_jvp_mask_free(attn_jvp_mask *m) {
+  if (!m) return;
+  free_device_schedules(m);
   delete m;
 }
 

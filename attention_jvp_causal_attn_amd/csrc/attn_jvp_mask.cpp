@@ -167,6 +167,43 @@ extern "C" int attn_jvp_mask_export(const attn_jvp_mask *m, int32_t *group_q_beg
 
 namespace attnjvp {
 
+int transpose_mask(const attn_jvp_mask *m, attn_jvp_mask **out) {
+  try {
+    // elementary key intervals: cut [0, n_k) at every range boundary
+    std::vector<int32_t> cuts = {0, m->n_k};
+    cuts.insert(cuts.end(), m->k_begin.begin(), m->k_begin.end());
+    cuts.insert(cuts.end(), m->k_end.begin(), m->k_end.end());
+    std::sort(cuts.begin(), cuts.end());
+    cuts.erase(std::unique(cuts.begin(), cuts.end()), cuts.end());
+    const size_t n_int = cuts.size() - 1;
+    // each interval collects the query ranges of the groups that admit it, in
+    // increasing query order (groups are visited in order)
+    std::vector<std::vector<std::pair<int32_t, int32_t>>> qr(n_int);
+    const size_t n_groups = m->group_q_begin.size() - 1;
+    for (size_t g = 0; g < n_groups; ++g) {
+      const std::pair<int32_t, int32_t> rows{m->group_q_begin[g], m->group_q_begin[g + 1]};
+      for (int32_t r = m->range_ptr[g]; r < m->range_ptr[g + 1]; ++r) {
+        const size_t a = std::lower_bound(cuts.begin(), cuts.end(), m->k_begin[r]) - cuts.begin();
+        const size_t b = std::lower_bound(cuts.begin(), cuts.end(), m->k_end[r]) - cuts.begin();
+        for (size_t i = a; i < b; ++i) {
+          if (!qr[i].empty() && qr[i].back().second == rows.first)
+            qr[i].back().second = rows.second;  // touching groups
+          else
+            qr[i].push_back(rows);
+        }
+      }
+    }
+    auto *t = new attn_jvp_mask();
+    t->n_q = m->n_k;
+    t->n_k = m->n_q;
+    finish_mask(t, cuts, qr);
+    *out = t;
+  } catch (const std::bad_alloc &) {
+    return ATTN_JVP_ERR_OOM;
+  }
+  return ATTN_JVP_OK;
+}
+
 // Classify every key block for every query tile.  A block is listed when some
 // row of the tile admits some key of it; it is full when every existing row
 // of the tile admits all block_n keys (so a block reaching past n_k is never
@@ -306,4 +343,9 @@ extern "C" int attn_jvp_mask_schedule(const attn_jvp_mask *m, int32_t block_m, i
   if (entry_partial) std::copy(s->entry_partial.begin(), s->entry_partial.end(), entry_partial);
   if (partial_bits) std::copy(s->partial_bits.begin(), s->partial_bits.end(), partial_bits);
   return ATTN_JVP_OK;
+}
+
+extern "C" int attn_jvp_mask_transpose(const attn_jvp_mask *m, attn_jvp_mask **out) {
+  if (!m || !out) return ATTN_JVP_ERR_NULL;
+  return attnjvp::transpose_mask(m, out);
 }

@@ -3,6 +3,7 @@
 
 #include <cstdint>
 #include <map>
+#include <memory>
 #include <mutex>
 #include <tuple>
 #include <vector>
@@ -95,9 +96,15 @@ struct attn_jvp_mask {
   mutable std::map<std::pair<int, int>, attnjvp::HostSchedule> host_sched;
   // (device, block_m, block_n) -> device copy
   mutable std::map<std::tuple<int, int, int>, attnjvp::DeviceSchedule> dev_sched;
+  // the transposed mask (keys as rows), built on first use by the backward
+  mutable std::unique_ptr<attn_jvp_mask> transposed;
 };
 
 namespace attnjvp {
+
+// The mask with query and key roles swapped: key j admits query i exactly
+// when query i admits key j.  Canonical like every other mask.
+int transpose_mask(const attn_jvp_mask *m, attn_jvp_mask **out);
 
 // Build (or fetch the cached) host schedule; caller holds m->mu.
 const HostSchedule *host_schedule_locked(const attn_jvp_mask *m, int block_m,

@@ -131,6 +131,13 @@ int attn_jvp_mask_schedule(const attn_jvp_mask *m, int32_t block_m,
                            int32_t *entry_block, int32_t *entry_partial,
                            uint32_t *partial_bits);
 
+/* The transposed mask: key and query roles swapped (its n_q is m's n_k):
+ * key j admits query i exactly when query i admits key j under m.  The
+ * backward pass walks it (key tiles over query blocks).  On success *out owns
+ * a new canonical mask; release it with attn_jvp_mask_free.
+ * Errors: ERR_NULL, ERR_OOM. */
+int attn_jvp_mask_transpose(const attn_jvp_mask *m, attn_jvp_mask **out);
+
 /* Release a mask and its device schedules.  The caller must make sure no
  * launched work still uses it (synchronise the streams first).  NULL is a
  * no-op. */

@@ -238,3 +238,38 @@ def test_canonical_merges():
     assert list(zip(kb, ke)) == [(0, 9)]
     d = aj.attn_jvp_mask_dense(7, 9)
     assert d.info() == dict(n_q=7, n_k=9, n_groups=1, n_ranges=1, n_visible_pairs=63)
+
+
+# ------------------------------------------------------------ transpose ----
+
+@pytest.mark.parametrize("nf,tpf,fpc", TF_CASES)
+def test_tf_transpose_is_matrix_transpose(nf, tpf, fpc):
+    m = aj.attn_jvp_mask_tf(nf, tpf, fpc)
+    t = aj.attn_jvp_mask_transpose(m)
+    N = 2 * nf * tpf
+    gq, rp, kb, ke = aj.attn_jvp_mask_export(t)
+    check_canonical(N, N, gq, rp, kb, ke)
+    np.testing.assert_array_equal(csr_to_matrix(N, N, gq, rp, kb, ke),
+                                  tf_allowed(nf, tpf, fpc).matrix().T)
+    assert t.info()["n_visible_pairs"] == m.info()["n_visible_pairs"]
+    # transposing twice gives back the canonical original
+    tt = aj.attn_jvp_mask_transpose(t)
+    for a, b in zip(aj.attn_jvp_mask_export(tt), aj.attn_jvp_mask_export(m)):
+        np.testing.assert_array_equal(a, b)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_rect_transpose_is_matrix_transpose(seed):
+    rng = np.random.default_rng(100 + seed)
+    n_q, n_k = int(rng.integers(1, 200)), int(rng.integers(1, 200))
+    gq, rp, kb, ke = random_rects(rng, n_q, n_k)
+    m = aj.attn_jvp_mask_rects(n_q, n_k, gq, rp, kb, ke)
+    t = aj.attn_jvp_mask_transpose(m)
+    info = t.info()
+    assert (info["n_q"], info["n_k"]) == (n_k, n_q)
+    egq, erp, ekb, eke = aj.attn_jvp_mask_export(t)
+    check_canonical(n_k, n_q, egq, erp, ekb, eke)
+    M = csr_to_matrix(n_q, n_k, *aj.attn_jvp_mask_export(m))
+    np.testing.assert_array_equal(csr_to_matrix(n_k, n_q, egq, erp, ekb, eke), M.T)
+    # the backward's key-tile schedule is the schedule of the transpose
+    check_schedule(t, M.T, 128, 32)
