@@ -241,3 +241,60 @@ def attn_jvp_fwd(q, k, v, dq, dk, dv, mask, scale=None, o=None, d_o=None, lse=No
         st = _lib.lib().attn_jvp_fwd(ctypes.byref(a), mask.handle, ctypes.c_void_p(handle))
     _check(st, "attn_jvp_fwd")
     return o, (d_o if tangent else None), lse
+
+
+def attn_jvp_bwd(q, k, v, o, g_o, lse, mask, scale=None, g_q=None, g_k=None, g_v=None,
+                 delta=None, stream=None):
+    """Gradients of sum(g_o * O) w.r.t. q, k, v for O = masked attention(q, k, v).
+
+    q, o, g_o: [B, n_q, H, D]; k, v: [B, n_k, H, D] bf16 device tensors with
+    the layout rules of attn_jvp_fwd; o and lse are the forward's outputs.
+    Outputs (allocated when not given): g_q like q, g_k and g_v like k, and
+    delta [B, H, n_q] fp32 (the row sums <g_o, o>).  Asynchronous on
+    ``stream``.  Returns (g_q, g_k, g_v, delta).
+    """
+    import torch
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("tensors must be [B, N, H, D]")
+    B, n_q, H, D = q.shape
+    n_k = k.shape[1]
+    for name, t, rows in (("k", k, n_k), ("v", v, n_k), ("o", o, n_q), ("g_o", g_o, n_q)):
+        if tuple(t.shape) != (B, rows, H, D):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {(B, rows, H, D)}")
+        if t.dtype != q.dtype or t.device != q.device:
+            raise ValueError(f"{name} differs from q in dtype or device")
+    if not q.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    for name, t in (("o", o), ("g_o", g_o)):
+        if t.stride() != q.stride():
+            raise ValueError(f"{name} must have the strides of q")
+    if v.stride() != k.stride():
+        raise ValueError("v must have the strides of k")
+    if tuple(lse.shape) != (B, H, n_q) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, n_q] tensor")
+    code = _dtype_code(q)
+    if g_q is None:
+        g_q = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
+    if g_k is None:
+        g_k = torch.empty_strided(k.shape, k.stride(), dtype=k.dtype, device=k.device)
+    if g_v is None:
+        g_v = torch.empty_strided(k.shape, k.stride(), dtype=k.dtype, device=k.device)
+    if delta is None:
+        delta = torch.empty((B, H, n_q), dtype=torch.float32, device=q.device)
+    if g_q.stride() != q.stride() or g_k.stride() != k.stride() or g_v.stride() != k.stride():
+        raise ValueError("g_q must have the strides of q, g_k and g_v those of k")
+    ptr = lambda t: t.data_ptr()
+    a = _lib.AttnJvpBwdArgs(
+        dtype=code, B=B, H=H, n_q=n_q, n_k=n_k, D=D,
+        q=ptr(q), k=ptr(k), v=ptr(v), o=ptr(o), g_o=ptr(g_o), lse=ptr(lse),
+        g_q=ptr(g_q), g_k=ptr(g_k), g_v=ptr(g_v), delta=ptr(delta),
+        q_stride_b=q.stride(0), q_stride_n=q.stride(1), q_stride_h=q.stride(2),
+        k_stride_b=k.stride(0), k_stride_n=k.stride(1), k_stride_h=k.stride(2),
+        scale=float(scale) if scale is not None else 0.0)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    with torch.cuda.device(q.device):
+        st = _lib.lib().attn_jvp_bwd(ctypes.byref(a), mask.handle, ctypes.c_void_p(handle))
+    _check(st, "attn_jvp_bwd")
+    return g_q, g_k, g_v, delta

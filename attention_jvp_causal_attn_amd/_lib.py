@@ -41,6 +41,17 @@ class AttnJvpArgs(ctypes.Structure):
     ]
 
 
+class AttnJvpBwdArgs(ctypes.Structure):
+    _fields_ = [
+        ("dtype", _i32), ("B", _i32), ("H", _i32), ("n_q", _i32), ("n_k", _i32), ("D", _i32),
+        ("q", _p), ("k", _p), ("v", _p), ("o", _p), ("g_o", _p), ("lse", _p),
+        ("g_q", _p), ("g_k", _p), ("g_v", _p), ("delta", _p),
+        ("q_stride_b", _i64), ("q_stride_n", _i64), ("q_stride_h", _i64),
+        ("k_stride_b", _i64), ("k_stride_n", _i64), ("k_stride_h", _i64),
+        ("scale", ctypes.c_float),
+    ]
+
+
 _PPMASK = ctypes.POINTER(ctypes.c_void_p)
 
 SIGNATURES = {
@@ -54,6 +65,7 @@ SIGNATURES = {
     "attn_jvp_mask_transpose": (_i32, [_p, _PPMASK]),
     "attn_jvp_mask_free": (None, [_p]),
     "attn_jvp_fwd": (_i32, [ctypes.POINTER(AttnJvpArgs), _p, _p]),
+    "attn_jvp_bwd": (_i32, [ctypes.POINTER(AttnJvpBwdArgs), _p, _p]),
     "attn_jvp_tile_shape": (_i32, [_i32, _i32, _pi32, _pi32]),
     "attn_jvp_status_str": (ctypes.c_char_p, [_i32]),
     "attn_jvp_version": (_i32, []),

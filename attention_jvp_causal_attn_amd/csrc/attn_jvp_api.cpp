@@ -1,6 +1,7 @@
 // C ABI entry points: argument validation, per-device schedule upload and
 // kernel dispatch.  Every tensor stays caller-owned device memory; the only
 // device memory the library owns is the per-mask tile schedule.
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 
@@ -118,20 +119,19 @@ extern "C" int attn_jvp_tile_shape(int32_t dtype, int32_t D, int32_t *block_m, i
 // of a group interleave the tile slots of each of its slices.  Needs the
 // slot count to split evenly over a group, else the identity map (which
 // interleaves slots over all 8 XCDs) is used.
-static void set_work_map(attnjvp::KernelParams &p) {
-  const int64_t S = int64_t(p.B) * p.H;
+static attnjvp::WorkMap make_work_map(int64_t slices, int32_t n_tiles) {
   int64_t g = 8;
-  while (S % g != 0) g /= 2;
+  while (slices % g != 0) g /= 2;
   const int m = int(8 / g);
-  if (p.n_tiles % m == 0) {
-    p.map_group = m;
-    p.map_slices = int(S / g);
-    p.map_slots = p.n_tiles / m;
-  } else {
-    p.map_group = 0;
-    p.map_slices = 0;
-    p.map_slots = 0;
-  }
+  if (n_tiles % m == 0) return {n_tiles, m, int32_t(slices / g), n_tiles / m};
+  return {n_tiles, 0, 0, 0};
+}
+
+static void set_work_map(attnjvp::KernelParams &p) {
+  const attnjvp::WorkMap w = make_work_map(int64_t(p.B) * p.H, p.n_tiles);
+  p.map_group = w.group;
+  p.map_slices = w.slices;
+  p.map_slots = w.slots;
 }
 
 extern "C" int attn_jvp_fwd(const attn_jvp_args *a, const attn_jvp_mask *m, void *stream) {
@@ -201,6 +201,86 @@ extern "C" int attn_jvp_fwd(const attn_jvp_args *a, const attn_jvp_mask *m, void
   set_work_map(p);
   int err = a->dtype == ATTN_JVP_BF16 ? attnjvp::launch_bf16(p, a->D, tangent, stream)
                                        : attnjvp::launch_f32(p, a->D, tangent, stream);
+  return err == hipSuccess ? ATTN_JVP_OK : ATTN_JVP_ERR_HIP;
+}
+
+extern "C" int attn_jvp_bwd(const attn_jvp_bwd_args *a, const attn_jvp_mask *m, void *stream) {
+  if (!a || !m) return ATTN_JVP_ERR_NULL;
+  if (a->dtype != ATTN_JVP_BF16 && a->dtype != ATTN_JVP_F32) return ATTN_JVP_ERR_DTYPE;
+  if (!a->q || !a->k || !a->v || !a->o || !a->g_o || !a->lse || !a->g_q || !a->g_k || !a->g_v ||
+      !a->delta)
+    return ATTN_JVP_ERR_NULL;
+  if (a->B <= 0 || a->H <= 0 || a->n_q <= 0 || a->n_k <= 0) return ATTN_JVP_ERR_SHAPE;
+  if (a->dtype != ATTN_JVP_BF16 || a->D != 128) return ATTN_JVP_ERR_UNSUPPORTED;
+  if (a->n_q != m->n_q || a->n_k != m->n_k) return ATTN_JVP_ERR_MASK;
+  if (!(std::isfinite(a->scale))) return ATTN_JVP_ERR_SHAPE;
+  if (int64_t(a->B) * a->H * std::max(a->n_q, a->n_k) > (int64_t(1) << 40)) return ATTN_JVP_ERR_SHAPE;
+  const int64_t es = 2;
+  const int64_t qs[3] = {a->q_stride_b, a->q_stride_n, a->q_stride_h};
+  const int64_t ks[3] = {a->k_stride_b, a->k_stride_n, a->k_stride_h};
+  for (int i = 0; i < 3; ++i) {
+    if (qs[i] < 0 || ks[i] < 0) return ATTN_JVP_ERR_SHAPE;
+    if ((qs[i] * es) % 16 || (ks[i] * es) % 16) return ATTN_JVP_ERR_ALIGN;
+  }
+  // 32-row blocks are addressed with 32-bit byte offsets
+  if (ks[1] * es * 32 > int64_t(0x7fffffff) || qs[1] * es * 32 > int64_t(0x7fffffff))
+    return ATTN_JVP_ERR_SHAPE;
+  if (a->H > 1 && (qs[2] < a->D || ks[2] < a->D)) return ATTN_JVP_ERR_SHAPE;
+  const void *ins[6] = {a->q, a->k, a->v, a->o, a->g_o, a->lse};
+  const void *outs[4] = {a->g_q, a->g_k, a->g_v, a->delta};
+  for (const void *p : ins)
+    if (!aligned16(p)) return ATTN_JVP_ERR_ALIGN;
+  for (const void *p : outs)
+    if (!aligned16(p)) return ATTN_JVP_ERR_ALIGN;
+  for (const void *p : ins)
+    for (const void *o : outs)
+      if (p == o) return ATTN_JVP_ERR_UNSUPPORTED;
+  for (int i = 0; i < 4; ++i)
+    for (int j = i + 1; j < 4; ++j)
+      if (outs[i] == outs[j]) return ATTN_JVP_ERR_UNSUPPORTED;
+
+  int device = -1;
+  if (hipGetDevice(&device) != hipSuccess) return ATTN_JVP_ERR_HIP;
+  const int BM = attnjvp::kBwdBlockM, BN = attnjvp::kBwdBlockN;
+  const DeviceSchedule *rs = nullptr, *cs = nullptr;
+  const attn_jvp_mask *t = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(m->mu);
+    int st = device_schedule_locked(m, device, BM, BN, &rs);
+    if (st != ATTN_JVP_OK) return st;
+    if (!m->transposed) {
+      attn_jvp_mask *tm = nullptr;
+      st = attnjvp::transpose_mask(m, &tm);
+      if (st != ATTN_JVP_OK) return st;
+      m->transposed.reset(tm);
+    }
+    t = m->transposed.get();
+  }
+  {
+    std::lock_guard<std::mutex> lock(t->mu);
+    int st = device_schedule_locked(t, device, BM, BN, &cs);
+    if (st != ATTN_JVP_OK) return st;
+  }
+  const int64_t slices = int64_t(a->B) * a->H;
+  if (int64_t(rs->n_tiles) * slices > int64_t(0x7fffffff) ||
+      int64_t(cs->n_tiles) * slices > int64_t(0x7fffffff))
+    return ATTN_JVP_ERR_SHAPE;
+
+  attnjvp::BwdParams p;
+  p.q = a->q; p.k = a->k; p.v = a->v; p.o = a->o; p.g_o = a->g_o; p.lse = a->lse;
+  p.g_q = a->g_q; p.g_k = a->g_k; p.g_v = a->g_v; p.delta = a->delta;
+  p.q_sb = a->q_stride_b; p.q_sn = a->q_stride_n; p.q_sh = a->q_stride_h;
+  p.k_sb = a->k_stride_b; p.k_sn = a->k_stride_n; p.k_sh = a->k_stride_h;
+  p.B = a->B; p.H = a->H; p.n_q = a->n_q; p.n_k = a->n_k;
+  p.scale = a->scale > 0.f ? a->scale : 1.0f / std::sqrt(float(a->D));
+  p.scale_log2 = float(double(p.scale) * 1.4426950408889634);
+  p.r_offsets = rs->tile_offsets; p.r_order = rs->tile_order; p.r_entries = rs->entries;
+  p.r_bits = rs->partial_bits; p.r_partial = rs->n_partial;
+  p.r_map = make_work_map(slices, rs->n_tiles);
+  p.c_offsets = cs->tile_offsets; p.c_order = cs->tile_order; p.c_entries = cs->entries;
+  p.c_bits = cs->partial_bits; p.c_partial = cs->n_partial;
+  p.c_map = make_work_map(slices, cs->n_tiles);
+  const int err = attnjvp::launch_bwd_bf16(p, a->D, stream);
   return err == hipSuccess ? ATTN_JVP_OK : ATTN_JVP_ERR_HIP;
 }
 

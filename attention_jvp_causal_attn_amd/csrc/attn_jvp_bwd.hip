@@ -1,0 +1,497 @@
+// Gradients of masked attention (the backward of the primal) for gfx950,
+// bf16 in and out, fp32 accumulate, head dim 128.
+//
+// The forward returns the row log-sum-exp so that a backward of the same
+// masked operator can reuse it ("Causal-rCM ..." summary, Appendix B: the
+// kernel's outputs are O, LSE and dO; the student is trained through the
+// TF-masked packed forward, Section 3).  With P_ij = exp(s_ij - LSE_i) over
+// the admissible pairs and g = dL/dO:
+//     D_i   = <g_i, O_i>
+//     dP_ij = <g_i, v_j>,   dS_ij = P_ij (dP_ij - D_i)
+//     dQ_i  = scale sum_j dS_ij k_j,   dK_j = scale sum_i dS_ij q_i,
+//     dV_j  = sum_i P_ij g_i.
+// Two passes, no atomics (deterministic):
+//  * dQ pass: a workgroup owns 128 query rows and walks the mask's schedule
+//    of admissible 32-key blocks: S^T = K Q^T and dP^T = V g^T (Q and g in
+//    registers as MFMA B operands, K and V from LDS), dS^T, then
+//    dQ^T += K^T dS^T with K^T read transposed from the same LDS tile.  It
+//    also computes D_i (from O and g) and stores it for the second pass;
+//  * dK/dV pass: a workgroup owns 128 keys and walks the schedule of the
+//    transposed mask (admissible 32-query blocks): S = Q K^T, dP = g V^T (K
+//    and V in registers, Q and g from LDS), then dV^T += g^T P and
+//    dK^T += Q^T dS.
+// Both passes use one lane per row (query or key) in each half-wave, the K-
+// row (or Q-row) permutation that puts a lane's 8 weights of a 16-wide step
+// in register order, direct-to-LDS copies into a 3-stage ring, and tiles
+// swizzled so that both row reads (ds_read_b128) and transposed reads
+// (ds_read_b64_tr_b16) hit distinct banks.
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+
+#include "internal.h"
+
+namespace attnjvp {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int D = 128;
+constexpr int kThreads = 256;
+constexpr int BM = kBwdBlockM;  // rows (or keys) per workgroup
+constexpr int BN = kBwdBlockN;  // keys (or queries) per block
+constexpr int kStages = 3;
+constexpr int KCH = D / 8;      // 16-byte chunks per row
+constexpr int KSTEPS = D / 16;
+constexpr int DT = D / 32;
+constexpr int kEntChunk = 512;
+constexpr int kChunksPerLane = BN * KCH / kThreads;  // per 32 x 128 tensor tile
+static_assert(BM == 128 && BN == 32 && kChunksPerLane * kThreads == BN * KCH, "tile shape");
+constexpr float kNegInf = -__builtin_inff();
+constexpr float kLog2e = 1.44269504088896340736f;
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 x) { return __builtin_bit_cast(bf16x8, x); }
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+__device__ __forceinline__ bf16x8 to_bf16x8(const float *x) {
+  const f32x8 v = {x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]};
+  return __builtin_convertvector(v, bf16x8);
+}
+__device__ __forceinline__ float xor32(float v) { return __shfl_xor(v, 32, 64); }
+
+// Bits 2 and 3 of a 32-row tile index swapped: the MFMA output element
+// (row 8j + 4h + i) of a tile whose A-operand rows are read in this order
+// holds row 16(j/2) + 8h + 4(j%2) + i, so lane-half h owns rows 16s + 8h + 0..7
+// of step s in register order.
+__device__ __forceinline__ int swap_bits23(int m) {
+  return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
+}
+// 16-byte-chunk XOR swizzle of a 256-byte row, conflict-free both for row
+// reads (16 lanes, 16 rows, one chunk: a bijection of the row's low 4 bits)
+// and for transposed reads (16 lanes, 4 consecutive rows x 32 bytes: the
+// rows land in 4 distinct 32-byte bank windows).
+__device__ __forceinline__ int sw(int row) { return 2 * (row & 7) | ((row >> 3) & 1); }
+
+// 16 bytes per lane straight into LDS at lds_wave + 16 * lane (lds_wave
+// wave-uniform); tracked by vmcnt and waited for explicitly.  One wait state
+// separates the M0 write from the copy.
+__device__ __forceinline__ void dma16(const void *base, uint32_t voff, uint32_t lds_wave) {
+  lds_wave = __builtin_amdgcn_readfirstlane(lds_wave);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(base), "s"(lds_wave)
+               : "memory", "m0");
+}
+// 4 bytes per lane from a per-lane address into LDS at lds_wave + 4 * lane.
+__device__ __forceinline__ void dma4(const void *addr, uint32_t lds_wave) {
+  lds_wave = __builtin_amdgcn_readfirstlane(lds_wave);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :
+               : "v"(addr), "s"(lds_wave)
+               : "memory", "m0");
+}
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Byte offset inside a 32-row block of copy chunk i of this lane (swizzled);
+// rows past the last valid one re-read it (masked out by the schedule).
+__device__ __forceinline__ uint32_t copy_offset(int i, int64_t row_stride, int rows_valid) {
+  const int qd = i * kThreads + int(threadIdx.x);
+  const int row = qd / KCH, pch = qd % KCH;
+  return uint32_t(min(row, rows_valid - 1)) * uint32_t(row_stride) * 2u +
+         uint32_t(pch ^ sw(row)) * 16u;
+}
+
+// Two 32 x 128 bf16 tiles (rows r0 .. r0+31 of a and b) plus the block's
+// 128 mask words into a stage at LDS st.
+__device__ __forceinline__ void copy_pair(uint32_t st, uint32_t a_at, uint32_t b_at,
+                                          uint32_t bits_at, int wave, const __bf16 *a,
+                                          const __bf16 *b, int64_t row_stride, int r0, int n_rows,
+                                          const uint32_t *bits_src) {
+  const int lane = threadIdx.x & 63;
+  const int64_t boff = int64_t(r0) * row_stride;
+  const int rows = min(BN, n_rows - r0);
+#pragma unroll
+  for (int i = 0; i < kChunksPerLane; ++i) {
+    const uint32_t off = copy_offset(i, row_stride, rows);
+    const uint32_t chunk = uint32_t(i * kThreads + wave * 64) * 16u;
+    dma16(a + boff, off, st + a_at + chunk);
+    dma16(b + boff, off, st + b_at + chunk);
+  }
+  // mask bits: BM words = 32 chunks; wave w copies chunks 8w .. 8w+7 (lanes 0..7)
+  if (lane < 8)
+    dma16(bits_src, uint32_t(wave * 8 + lane) * 16u, st + bits_at + uint32_t(wave) * 128u);
+}
+
+// A-operand row read of a swizzled 32 x 128 tile: this lane's row (permuted)
+// at k-step t.
+__device__ __forceinline__ bf16x8 row_operand(const uint4 *tile, int prow, int t, int hh) {
+  return as_bf16x8(tile[prow * KCH + ((2 * t + hh) ^ sw(prow))]);
+}
+
+// A-operand transposed read of a swizzled 32 x 128 tile for step s of 16
+// rows and dim tile nt: within each 16-lane group, lane jl reads row
+// (16s + 4*half + krel) at dims (d0 + 4*(jl%4)) .. +3.
+__device__ __forceinline__ bf16x8 tr_operand(const uint4 *tile, int s, int nt, int dcol, int krel) {
+  bf16x4 h[2];
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int row = 16 * s + 4 * half + krel;
+    const int d = 32 * nt + dcol;
+    const int chunk = row * KCH + ((d >> 3) ^ sw(row));
+    const char *ptr = reinterpret_cast<const char *>(tile + chunk) + (d & 7) * 2;
+    h[half] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4 *)(ptr));
+  }
+  return __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Register-order position of element r of a 16-wide half-tile: row (or
+// column) 16(j/2) + 8h + 4(j%2) + i for r = 4j + i; shifted by 8h, the bit of a
+// 32-bit mask word.
+__device__ __forceinline__ int reg_pos(int r) {
+  const int j = r >> 2, i = r & 3;
+  return 16 * (j >> 1) + 4 * (j & 1) + i;
+}
+
+// ---------------------------------------------------------------- dQ pass
+
+struct alignas(16) KVTile {
+  uint4 k[BN * KCH];
+  uint4 v[BN * KCH];
+  uint32_t bits[BM];
+};
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_dq_kernel(BwdParams p) {
+  __shared__ KVTile ring[kStages];
+  __shared__ int2 ents[2][kEntChunk];
+  const int L = work_item(int(blockIdx.x), p.r_map);
+  const int slot = L % p.r_map.n_tiles;
+  const int bh = L / p.r_map.n_tiles;
+  const int head = bh % p.H, batch = bh / p.H;
+  const int tile = p.r_order[slot];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 31, hh = lane >> 5;
+  const int row_in_tile = wave * 32 + col;
+  const int qrow = tile * BM + row_in_tile;
+  const bool qvalid = qrow < p.n_q;
+  const uint32_t ring_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&ring[0]));
+  auto stage_lds = [&](int s) { return ring_lds + uint32_t(s) * uint32_t(sizeof(KVTile)); };
+
+  const int64_t koff = int64_t(batch) * p.k_sb + int64_t(head) * p.k_sh;
+  const __bf16 *kb = static_cast<const __bf16 *>(p.k) + koff;
+  const __bf16 *vb = static_cast<const __bf16 *>(p.v) + koff;
+  const int64_t qoff = int64_t(batch) * p.q_sb + int64_t(head) * p.q_sh;
+  const int64_t lrow = (int64_t(batch) * p.H + head) * p.n_q;
+
+  const int e0 = p.r_offsets[tile], e1 = p.r_offsets[tile + 1];
+  const int n = e1 - e0;
+  auto load_entries = [&](int c) {
+    int2 *dst = ents[c & 1];
+    const int base = e0 + c * kEntChunk;
+    for (int i = threadIdx.x; i < kEntChunk; i += kThreads)
+      dst[i] = base + i < e1 ? p.r_entries[base + i] : make_int2(0, -1);
+  };
+  auto entry = [&](int j) {
+    const int2 e = ents[(j / kEntChunk) & 1][j % kEntChunk];
+    return make_int2(__builtin_amdgcn_readfirstlane(e.x), __builtin_amdgcn_readfirstlane(e.y));
+  };
+  auto bits_of = [&](int2 e) { return p.r_bits + int64_t(e.y >= 0 ? e.y : p.r_partial) * BM; };
+  auto issue = [&](int s, int2 e) {
+    copy_pair(stage_lds(s), offsetof(KVTile, k), offsetof(KVTile, v), offsetof(KVTile, bits), wave,
+              kb, vb, p.k_sn, e.x * BN, p.n_k, bits_of(e));
+  };
+
+  load_entries(0);
+  __syncthreads();
+  if (n > 0) issue(0, entry(0));
+
+  // Q and g rows as B operands; D_i = <g_i, O_i>; the row's LSE in log2 units
+  bf16x8 qf[KSTEPS], gf[KSTEPS];
+  float dsum = 0.f;
+  {
+    const int qr = qvalid ? qrow : 0;
+    const int64_t off = qoff + int64_t(qr) * p.q_sn + 8 * hh;
+    const __bf16 *qb = static_cast<const __bf16 *>(p.q) + off;
+    const __bf16 *gb = static_cast<const __bf16 *>(p.g_o) + off;
+    const __bf16 *ob = static_cast<const __bf16 *>(p.o) + off;
+#pragma unroll
+    for (int t = 0; t < KSTEPS; ++t) {
+      qf[t] = as_bf16x8(*reinterpret_cast<const uint4 *>(qb + 16 * t));
+      gf[t] = as_bf16x8(*reinterpret_cast<const uint4 *>(gb + 16 * t));
+      const bf16x8 of = as_bf16x8(*reinterpret_cast<const uint4 *>(ob + 16 * t));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dsum = __builtin_fmaf(float(gf[t][e]), float(of[e]), dsum);
+    }
+  }
+  dsum += xor32(dsum);
+  const float lse2 = qvalid ? p.lse[lrow + qrow] * kLog2e : 0.f;
+  if (qvalid && hh == 0) p.delta[lrow + qrow] = dsum;
+  wait_vmcnt<0>();
+  if (n > 1) issue(1, entry(1));
+
+  f32x16 acc[DT];
+#pragma unroll
+  for (int nt = 0; nt < DT; ++nt) acc[nt] = f32x16{};
+  const int krow = swap_bits23(col);
+  const int g16 = lane >> 4, jl = lane & 15;
+  const int dcol = 16 * (g16 & 1) + 4 * (jl & 3);
+  const int krel = 8 * hh + (jl >> 2);
+  const float sl2 = p.scale_log2;
+
+  int cur = 0;
+  for (int j = 0; j < n; ++j) {
+    if ((j + 2) % kEntChunk == 0 && j + 2 < n) load_entries((j + 2) / kEntChunk);
+    if (j + 1 < n)
+      wait_vmcnt<2 * kChunksPerLane + 1>();
+    else
+      wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (j + 2 < n) issue(cur >= 1 ? cur - 1 : cur + 2, entry(j + 2));
+    const KVTile *st = &ring[cur];
+    const int2 ent = entry(j);
+
+    f32x16 S = {}, G = {};
+#pragma unroll
+    for (int t = 0; t < KSTEPS; ++t) {
+      S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand(st->k, krow, t, hh), qf[t], S, 0, 0, 0);
+      G = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand(st->v, krow, t, hh), gf[t], G, 0, 0, 0);
+    }
+    const uint32_t bits = ent.y >= 0 ? st->bits[row_in_tile] >> (8 * hh) : ~0u;
+    float gs[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const bool ok = (bits >> reg_pos(r)) & 1u;
+      const float pr = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], sl2, -lse2)) : 0.f;
+      gs[r] = pr * (G[r] - dsum);
+    }
+    bf16x8 gsb[2];
+    gsb[0] = to_bf16x8(gs);
+    gsb[1] = to_bf16x8(gs + 8);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+#pragma unroll
+      for (int nt = 0; nt < DT; ++nt)
+        acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(st->k, s, nt, dcol, krel),
+                                                          gsb[s], acc[nt], 0, 0, 0);
+    }
+    cur = cur == kStages - 1 ? 0 : cur + 1;
+  }
+
+  if (!qvalid) return;
+  __bf16 *out = static_cast<__bf16 *>(p.g_q) + qoff + int64_t(qrow) * p.q_sn;
+#pragma unroll
+  for (int nt = 0; nt < DT; ++nt) {
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int d0 = 32 * nt + 8 * jj + 4 * hh;
+      float x[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = acc[nt][4 * jj + i] * p.scale;
+      *reinterpret_cast<uint2 *>(out + d0) = make_uint2(pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]));
+    }
+  }
+}
+
+// ------------------------------------------------------------ dK/dV pass
+
+struct alignas(16) QGTile {
+  uint4 q[BN * KCH];
+  uint4 g[BN * KCH];
+  float ld[4 * 16];  // wave w's region: LSE of queries 8w .. 8w+7, then their D
+  uint32_t bits[BM];
+};
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_dkv_kernel(BwdParams p) {
+  __shared__ QGTile ring[kStages];
+  __shared__ int2 ents[2][kEntChunk];
+  const int L = work_item(int(blockIdx.x), p.c_map);
+  const int slot = L % p.c_map.n_tiles;
+  const int bh = L / p.c_map.n_tiles;
+  const int head = bh % p.H, batch = bh / p.H;
+  const int tile = p.c_order[slot];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 31, hh = lane >> 5;
+  const int key_in_tile = wave * 32 + col;
+  const int krow_g = tile * BM + key_in_tile;
+  const bool kvalid = krow_g < p.n_k;
+  const uint32_t ring_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&ring[0]));
+  auto stage_lds = [&](int s) { return ring_lds + uint32_t(s) * uint32_t(sizeof(QGTile)); };
+
+  const int64_t qoff = int64_t(batch) * p.q_sb + int64_t(head) * p.q_sh;
+  const __bf16 *qb = static_cast<const __bf16 *>(p.q) + qoff;
+  const __bf16 *gb = static_cast<const __bf16 *>(p.g_o) + qoff;
+  const int64_t koff = int64_t(batch) * p.k_sb + int64_t(head) * p.k_sh;
+  const int64_t lrow = (int64_t(batch) * p.H + head) * p.n_q;
+
+  const int e0 = p.c_offsets[tile], e1 = p.c_offsets[tile + 1];
+  const int n = e1 - e0;
+  auto load_entries = [&](int c) {
+    int2 *dst = ents[c & 1];
+    const int base = e0 + c * kEntChunk;
+    for (int i = threadIdx.x; i < kEntChunk; i += kThreads)
+      dst[i] = base + i < e1 ? p.c_entries[base + i] : make_int2(0, -1);
+  };
+  auto entry = [&](int j) {
+    const int2 e = ents[(j / kEntChunk) & 1][j % kEntChunk];
+    return make_int2(__builtin_amdgcn_readfirstlane(e.x), __builtin_amdgcn_readfirstlane(e.y));
+  };
+  auto bits_of = [&](int2 e) { return p.c_bits + int64_t(e.y >= 0 ? e.y : p.c_partial) * BM; };
+  auto issue = [&](int s, int2 e) {
+    const int q0 = e.x * BN;
+    copy_pair(stage_lds(s), offsetof(QGTile, q), offsetof(QGTile, g), offsetof(QGTile, bits), wave,
+              qb, gb, p.q_sn, q0, p.n_q, bits_of(e));
+    // LSE and D of queries q0 + 8w .. q0 + 8w + 7 (lanes 0..7, 8..15), clamped
+    if (lane < 16) {
+      const int qi = min(q0 + 8 * wave + (lane & 7), p.n_q - 1);
+      const float *src = lane < 8 ? p.lse + lrow + qi : p.delta + lrow + qi;
+      dma4(src, stage_lds(s) + uint32_t(offsetof(QGTile, ld)) + uint32_t(wave) * 64u);
+    }
+  };
+
+  load_entries(0);
+  __syncthreads();
+  if (n > 0) issue(0, entry(0));
+
+  // K and V rows as B operands
+  bf16x8 kf[KSTEPS], vf[KSTEPS];
+  {
+    const int kr = kvalid ? krow_g : 0;
+    const int64_t off = koff + int64_t(kr) * p.k_sn + 8 * hh;
+    const __bf16 *kp = static_cast<const __bf16 *>(p.k) + off;
+    const __bf16 *vp = static_cast<const __bf16 *>(p.v) + off;
+#pragma unroll
+    for (int t = 0; t < KSTEPS; ++t) {
+      kf[t] = as_bf16x8(*reinterpret_cast<const uint4 *>(kp + 16 * t));
+      vf[t] = as_bf16x8(*reinterpret_cast<const uint4 *>(vp + 16 * t));
+    }
+  }
+  wait_vmcnt<0>();
+  if (n > 1) issue(1, entry(1));
+
+  f32x16 accK[DT], accV[DT];
+#pragma unroll
+  for (int nt = 0; nt < DT; ++nt) {
+    accK[nt] = f32x16{};
+    accV[nt] = f32x16{};
+  }
+  const int qperm = swap_bits23(col);
+  const int g16 = lane >> 4, jl = lane & 15;
+  const int dcol = 16 * (g16 & 1) + 4 * (jl & 3);
+  const int krel = 8 * hh + (jl >> 2);
+  const float sl2 = p.scale_log2;
+
+  int cur = 0;
+  for (int j = 0; j < n; ++j) {
+    if ((j + 2) % kEntChunk == 0 && j + 2 < n) load_entries((j + 2) / kEntChunk);
+    if (j + 1 < n)
+      wait_vmcnt<2 * kChunksPerLane + 2>();
+    else
+      wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (j + 2 < n) issue(cur >= 1 ? cur - 1 : cur + 2, entry(j + 2));
+    const QGTile *st = &ring[cur];
+    const int2 ent = entry(j);
+
+    f32x16 S = {}, G = {};
+#pragma unroll
+    for (int t = 0; t < KSTEPS; ++t) {
+      S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand(st->q, qperm, t, hh), kf[t], S, 0, 0, 0);
+      G = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand(st->g, qperm, t, hh), vf[t], G, 0, 0, 0);
+    }
+    // LSE and D of this lane's 16 queries: 8hh + 0..7 and 16 + 8hh + 0..7
+    float lq[16], dq[16];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const float4 *reg = reinterpret_cast<const float4 *>(st->ld + 16 * (2 * half + hh));
+      const float4 a = reg[0], b = reg[1], c = reg[2], d = reg[3];
+      const float la[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+      const float da[8] = {c.x, c.y, c.z, c.w, d.x, d.y, d.z, d.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        lq[8 * half + e] = la[e];
+        dq[8 * half + e] = da[e];
+      }
+    }
+    const uint32_t bits = ent.y >= 0 ? st->bits[key_in_tile] >> (8 * hh) : ~0u;
+    float pr[16], gs[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int pos = reg_pos(r);               // query 8hh + pos of the block
+      const int e = 8 * (pos >> 4) + (pos & 7);  // its slot in lq / dq
+      const bool ok = (bits >> pos) & 1u;
+      pr[r] = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], sl2, -lq[e] * kLog2e)) : 0.f;
+      gs[r] = pr[r] * (G[r] - dq[e]);
+    }
+    bf16x8 pb[2], gsb[2];
+    pb[0] = to_bf16x8(pr);
+    pb[1] = to_bf16x8(pr + 8);
+    gsb[0] = to_bf16x8(gs);
+    gsb[1] = to_bf16x8(gs + 8);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+#pragma unroll
+      for (int nt = 0; nt < DT; ++nt) {
+        accV[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(st->g, s, nt, dcol, krel),
+                                                           pb[s], accV[nt], 0, 0, 0);
+        accK[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(st->q, s, nt, dcol, krel),
+                                                           gsb[s], accK[nt], 0, 0, 0);
+      }
+    }
+    cur = cur == kStages - 1 ? 0 : cur + 1;
+  }
+
+  if (!kvalid) return;
+  const int64_t ooff = koff + int64_t(krow_g) * p.k_sn;
+  __bf16 *gk = static_cast<__bf16 *>(p.g_k) + ooff;
+  __bf16 *gv = static_cast<__bf16 *>(p.g_v) + ooff;
+#pragma unroll
+  for (int nt = 0; nt < DT; ++nt) {
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int d0 = 32 * nt + 8 * jj + 4 * hh;
+      float xk[4], xv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        xk[i] = accK[nt][4 * jj + i] * p.scale;
+        xv[i] = accV[nt][4 * jj + i];
+      }
+      *reinterpret_cast<uint2 *>(gk + d0) = make_uint2(pack_bf16(xk[0], xk[1]), pack_bf16(xk[2], xk[3]));
+      *reinterpret_cast<uint2 *>(gv + d0) = make_uint2(pack_bf16(xv[0], xv[1]), pack_bf16(xv[2], xv[3]));
+    }
+  }
+}
+
+}  // namespace
+
+int launch_bwd_bf16(const BwdParams &p, int D_, void *stream) {
+  if (D_ != D) return hipErrorInvalidValue;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t Gq = int64_t(p.r_map.n_tiles) * p.B * p.H;
+  const int64_t Gk = int64_t(p.c_map.n_tiles) * p.B * p.H;
+  // the dQ pass stores D, which the dK/dV pass reads: same stream, in order
+  hipLaunchKernelGGL(bwd_dq_kernel, dim3(unsigned(Gq)), dim3(kThreads), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_dkv_kernel, dim3(unsigned(Gk)), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace attnjvp

@@ -67,18 +67,55 @@ struct KernelParams {
   int32_t map_slots;
 };
 
+// One grid's workgroup -> work item map (see work_item).
+struct WorkMap {
+  int32_t n_tiles;  // tiles per (batch, head) slice
+  int32_t group;    // 0: identity map
+  int32_t slices;
+  int32_t slots;
+};
+
+// Everything the two backward launches need, passed by value.  The dQ pass
+// walks query tiles over key blocks (the mask's schedule); the dK/dV pass
+// walks key tiles over query blocks (the schedule of the transposed mask).
+struct BwdParams {
+  const void *q, *k, *v, *o, *g_o;
+  const float *lse;
+  void *g_q, *g_k, *g_v;
+  float *delta;
+  int64_t q_sb, q_sn, q_sh;
+  int64_t k_sb, k_sn, k_sh;
+  int32_t B, H, n_q, n_k;
+  float scale, scale_log2;
+  // query tiles x key blocks
+  const int32_t *r_offsets, *r_order;
+  const int2 *r_entries;
+  const uint32_t *r_bits;  // r_partial blocks, then one all-ones block
+  int32_t r_partial;
+  WorkMap r_map;
+  // key tiles x query blocks
+  const int32_t *c_offsets, *c_order;
+  const int2 *c_entries;
+  const uint32_t *c_bits;  // c_partial blocks, then one all-ones block
+  int32_t c_partial;
+  WorkMap c_map;
+};
+
 #if defined(__HIP__)
 // Workgroup w is dispatched to XCD w % 8 (its position in that XCD's stream
 // is w / 8).  Returns the work item (slice * n_tiles + slot) of w: each XCD
 // receives an equal share of work (interleaved heavy-first slots) and the
 // workgroups resident on one XCD at a time belong to the same slice, so they
 // stream the same key blocks through that XCD's L2.
-__device__ __forceinline__ int work_item(int w, const KernelParams &p) {
-  if (p.map_group == 0) return w;
+__device__ __forceinline__ int work_item(int w, const WorkMap &m) {
+  if (m.group == 0) return w;
   const int x = w & 7, local = w >> 3;
-  const int grp = x / p.map_group, mem = x % p.map_group;
-  const int sl = local / p.map_slots, k = local % p.map_slots;
-  return (grp * p.map_slices + sl) * p.n_tiles + mem + k * p.map_group;
+  const int grp = x / m.group, mem = x % m.group;
+  const int sl = local / m.slots, k = local % m.slots;
+  return (grp * m.slices + sl) * m.n_tiles + mem + k * m.group;
+}
+__device__ __forceinline__ int work_item(int w, const KernelParams &p) {
+  return work_item(w, WorkMap{p.n_tiles, p.map_group, p.map_slices, p.map_slots});
 }
 #endif
 
@@ -113,12 +150,15 @@ const HostSchedule *host_schedule_locked(const attn_jvp_mask *m, int block_m,
 // Kernel launchers (defined in the .hip files).  Return a hipError_t value.
 int launch_bf16(const KernelParams &p, int D, bool tangent, void *stream);
 int launch_bf16_wide(const KernelParams &p, bool tangent, void *stream);  // D = 128
+int launch_bwd_bf16(const BwdParams &p, int D, void *stream);
 int launch_f32(const KernelParams &p, int D, bool tangent, void *stream);
 
 // Tile shapes of the kernels.
 constexpr int kBf16BlockM = 128;      // head dim 64: 4 waves x 32 rows
 constexpr int kBf16BlockMWide = 256;  // head dim 128: 8 waves x 32 rows
 constexpr int kBf16BlockN = 32;
+constexpr int kBwdBlockM = 128;       // backward: 4 waves x 32 rows (or keys)
+constexpr int kBwdBlockN = 32;        // backward: blocks of 32 keys (or queries)
 constexpr int kF32BlockM = 64;
 constexpr int kF32BlockN = 32;
 

@@ -177,6 +177,40 @@ typedef struct attn_jvp_args {
 int attn_jvp_fwd(const attn_jvp_args *a, const attn_jvp_mask *m,
                  void *hip_stream);
 
+/* Arguments of one backward call: the gradients of L = sum(g_o * O) with
+ * respect to Q, K and V for the masked attention O = attn(Q, K, V) of the
+ * forward (the forward returns LSE so that this pass can reuse it).
+ * Layouts as in attn_jvp_args: Q, O, g_o, g_q use the q_stride_* strides and
+ * n_q rows; K, V, g_k, g_v the k_stride_* strides and n_k rows; lse (input,
+ * the forward's) and delta (output) are [B, H, n_q] fp32, contiguous.  delta
+ * receives D_i = <g_o_i, O_i>, the row sums the pass needs; it is returned so
+ * the caller owns all memory.  Every pointer and stride in bytes a multiple
+ * of 16; outputs alias nothing.  Supported: dtype ATTN_JVP_BF16, D = 128. */
+typedef struct attn_jvp_bwd_args {
+  int32_t dtype;
+  int32_t B, H;
+  int32_t n_q, n_k;     /* must equal the mask's */
+  int32_t D;
+  const void *q, *k, *v;
+  const void *o;        /* the forward's output O */
+  const void *g_o;      /* gradient flowing into O */
+  const float *lse;     /* the forward's LSE (natural log) */
+  void *g_q, *g_k, *g_v;
+  float *delta;
+  int64_t q_stride_b, q_stride_n, q_stride_h;
+  int64_t k_stride_b, k_stride_n, k_stride_h;
+  float scale;          /* the forward's scale; <= 0 selects 1/sqrt(D) */
+} attn_jvp_bwd_args;
+
+/* Launch the backward on hip_stream: a dQ pass over query tiles (which also
+ * writes delta) then a dK/dV pass over key tiles of the transposed mask
+ * (built and uploaded on first use, cached with the mask).  Asynchronous,
+ * deterministic (no atomics).  Errors: ERR_NULL, ERR_DTYPE, ERR_SHAPE,
+ * ERR_ALIGN, ERR_MASK, ERR_UNSUPPORTED (dtype other than bf16, D other than
+ * 128, aliasing), ERR_HIP, ERR_OOM. */
+int attn_jvp_bwd(const attn_jvp_bwd_args *a, const attn_jvp_mask *m,
+                 void *hip_stream);
+
 /* Tile shape (query rows, keys) the kernel for (dtype, D) uses; these are the
  * block_m / block_n of its schedule.  Errors: ERR_NULL, ERR_DTYPE,
  * ERR_UNSUPPORTED (D not 64 or 128). */

@@ -127,3 +127,48 @@ def test_python_binding_requires_gpu_tensors():
         aj.attn_jvp_fwd(x, x, x, x, x, x, mask)
     with pytest.raises(ValueError):
         aj.attn_jvp_fwd(x, x, x, x, None, x, mask)
+
+
+def _bwd_args(mask, **kw):
+    info = mask.info()
+    base = dict(dtype=0, B=1, H=2, n_q=info["n_q"], n_k=info["n_k"], D=128,
+                q=0x10000, k=0x20000, v=0x30000, o=0x40000, g_o=0x50000, lse=0x60000,
+                g_q=0x70000, g_k=0x80000, g_v=0x90000, delta=0xa0000,
+                q_stride_b=0, q_stride_n=256, q_stride_h=128,
+                k_stride_b=0, k_stride_n=256, k_stride_h=128, scale=0.0)
+    base.update(kw)
+    return _lib.AttnJvpBwdArgs(**base)
+
+
+BAD_BWD = [
+    (dict(dtype=5), _lib.ATTN_JVP_ERR_DTYPE),
+    (dict(q=None), _lib.ATTN_JVP_ERR_NULL),
+    (dict(o=None), _lib.ATTN_JVP_ERR_NULL),
+    (dict(lse=None), _lib.ATTN_JVP_ERR_NULL),
+    (dict(delta=None), _lib.ATTN_JVP_ERR_NULL),
+    (dict(g_v=None), _lib.ATTN_JVP_ERR_NULL),
+    (dict(dtype=1), _lib.ATTN_JVP_ERR_UNSUPPORTED),
+    (dict(D=64), _lib.ATTN_JVP_ERR_UNSUPPORTED),
+    (dict(B=0), _lib.ATTN_JVP_ERR_SHAPE),
+    (dict(n_k=11), _lib.ATTN_JVP_ERR_MASK),
+    (dict(g_q=0x70008), _lib.ATTN_JVP_ERR_ALIGN),
+    (dict(k_stride_n=257), _lib.ATTN_JVP_ERR_ALIGN),
+    (dict(q_stride_h=64), _lib.ATTN_JVP_ERR_SHAPE),
+    (dict(g_q=0x10000), _lib.ATTN_JVP_ERR_UNSUPPORTED),   # output aliases q
+    (dict(g_v=0x80000), _lib.ATTN_JVP_ERR_UNSUPPORTED),   # g_v aliases g_k
+    (dict(scale=float("nan")), _lib.ATTN_JVP_ERR_SHAPE),
+]
+
+
+@pytest.mark.parametrize("kw,status", BAD_BWD)
+def test_bwd_rejects_bad_arguments(kw, status):
+    mask = aj.attn_jvp_mask_tf(4, 16, 1)
+    a = _bwd_args(mask, **kw)
+    assert _lib.lib().attn_jvp_bwd(ctypes.byref(a), mask.handle, None) == status
+
+
+@pytest.mark.skipif(_gpu_present(), reason="needs a host without a HIP device")
+def test_bwd_without_device_reports_hip_error():
+    mask = aj.attn_jvp_mask_tf(4, 16, 1)
+    a = _bwd_args(mask)
+    assert _lib.lib().attn_jvp_bwd(ctypes.byref(a), mask.handle, None) == _lib.ATTN_JVP_ERR_HIP

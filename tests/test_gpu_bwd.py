@@ -1,0 +1,135 @@
+"""GPU parity of the backward (gradients of the masked primal) against the
+fp64 oracle, through the C ABI.  The GPU backward consumes the GPU forward's
+O and LSE; the oracle sees only the seeded inputs.  Tolerance per output
+tensor: max|gpu - ref| <= 2e-2 * max|ref| (bf16 inputs and outputs)."""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import attention_jvp_causal_attn_amd as aj
+from attention_jvp_causal_attn_amd.inputs import WORKLOADS, make_inputs, make_random
+from oracle import dense_allowed, masked_attention_grad, rects_allowed, tf_allowed
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-2
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def f64(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def check(name, got, ref, tol=TOL):
+    got = np.asarray(got, dtype=np.float64)
+    assert np.isfinite(got).all(), f"{name}: non-finite values"
+    err = np.abs(got - ref).max()
+    scale = np.abs(ref).max()
+    rel = err / scale if scale > 0 else err
+    say(f"  {name}: max|err| = {err:.3e}, max|ref| = {scale:.3e}, ratio = {rel:.3e} (tol {tol})")
+    assert rel <= tol, f"{name}: {rel:.3e} > {tol}"
+
+
+def run_bwd(x, g, mask):
+    xd = {k: v.cuda() for k, v in x.items()}
+    gd = g.cuda()
+    o, _, lse = aj.attn_jvp_fwd(xd["q"], xd["k"], xd["v"], None, None, None, mask)
+    gq, gk, gv, delta = aj.attn_jvp_bwd(xd["q"], xd["k"], xd["v"], o, gd, lse, mask)
+    torch.cuda.synchronize()
+    return gq, gk, gv, delta
+
+
+def parity(x, g, pred, mask, rows=None, keys=None):
+    gq, gk, gv, delta = run_bwd(x, g, mask)
+    dQ, dK, dV, Ds = masked_attention_grad(x["q"], x["k"], x["v"], g, pred, rows=rows, keys=keys)
+    rsel = slice(None) if rows is None else torch.as_tensor(rows)
+    ksel = slice(None) if keys is None else torch.as_tensor(keys)
+    check("dQ", f64(gq[:, rsel]), dQ)
+    check("dK", f64(gk[:, ksel]), dK)
+    check("dV", f64(gv[:, ksel]), dV)
+    check("D", f64(delta[:, :, rsel]), Ds)
+
+
+SMALL = [
+    (5, 37, 1, 2, 3),   # N=370: 3 query tiles, ragged tail, unaligned units
+    (4, 64, 1, 1, 2),   # tile-aligned units
+    (3, 100, 3, 2, 1),  # one chunk of 300 tokens per stream
+    (2, 1, 1, 1, 1),    # N=4: rows with a single admissible key
+    (9, 33, 3, 1, 1),
+]
+
+
+@pytest.mark.parametrize("nf,tpf,fpc,B,H", SMALL)
+def test_small_tf_bwd(nf, tpf, fpc, B, H):
+    say(f"case: bwd bf16 TF nf={nf} tpf={tpf} fpc={fpc} B={B} H={H}")
+    pred = tf_allowed(nf, tpf, fpc)
+    x = make_random(B, pred.n_q, H, 128, dtype="bf16", seed=9500 + nf * 10 + tpf)
+    g = make_random(B, pred.n_q, H, 128, dtype="bf16", seed=9600 + nf)["q"]
+    parity(x, g, pred, aj.attn_jvp_mask_tf(nf, tpf, fpc))
+
+
+def test_rect_bwd_queries_differ_from_keys():
+    # queries of the current chunk against a longer key sequence, with keys
+    # that no query sees (their gradients are zero)
+    n_q, n_k = 150, 420
+    rects = [(0, 70, 0, 300), (70, 150, 0, 140), (70, 150, 260, 330)]
+    gq = [0, 70, 150]
+    rp = [0, 1, 3]
+    kb = [0, 0, 260]
+    ke = [300, 140, 330]
+    pred = rects_allowed(n_q, n_k, rects)
+    mask = aj.attn_jvp_mask_rects(n_q, n_k, gq, rp, kb, ke)
+    xq = make_random(1, n_q, 2, 128, dtype="bf16", seed=9700)
+    xk = make_random(1, n_k, 2, 128, dtype="bf16", seed=9710)
+    x = {"q": xq["q"], "k": xk["k"], "v": xk["v"]}
+    g = xq["dq"]
+    gq_, gk_, gv_, _ = run_bwd(x, g, mask)
+    assert torch.count_nonzero(gk_[:, 330:]) == 0 and torch.count_nonzero(gv_[:, 330:]) == 0
+    parity(x, g, pred, mask)
+
+
+def test_dense_bwd():
+    pred = dense_allowed(300, 300)
+    x = make_random(2, 300, 2, 128, dtype="bf16", seed=9800)
+    g = make_random(2, 300, 2, 128, dtype="bf16", seed=9810)["q"]
+    parity(x, g, pred, aj.attn_jvp_mask_dense(300, 300))
+
+
+def test_bwd_deterministic():
+    pred = tf_allowed(4, 50, 2)
+    x = make_random(1, pred.n_q, 2, 128, dtype="bf16", seed=9900)
+    g = make_random(1, pred.n_q, 2, 128, dtype="bf16", seed=9910)["q"]
+    mask = aj.attn_jvp_mask_tf(4, 50, 2)
+    a = run_bwd(x, g, mask)
+    b = run_bwd(x, g, mask)
+    for u, w in zip(a, b):
+        assert torch.equal(u, w)
+
+
+def test_full_size_batched_workload_bwd_sampled():
+    # batched 22k workload with outlier rows, one (b, h) slice checked on
+    # sampled rows (dQ) and sampled keys (dK, dV) against the oracle
+    w = WORKLOADS[4]
+    say(f"case: bwd {w.describe()}")
+    x = make_inputs(w)
+    g = make_random(w.B, w.N, w.H, w.D, dtype=w.dtype, seed=9950)["q"]
+    mask = aj.attn_jvp_mask_tf(w.n_frames, w.tokens_per_frame, w.frames_per_chunk)
+    gq, gk, gv, delta = run_bwd(x, g, mask)
+    pred = tf_allowed(w.n_frames, w.tokens_per_frame, w.frames_per_chunk)
+    rng = np.random.default_rng(5)
+    rows = np.sort(rng.choice(w.N, size=48, replace=False))
+    keys = np.sort(rng.choice(w.N, size=48, replace=False))
+    b, h = 1, 5
+    sl = {k: v[b:b + 1, :, h:h + 1] for k, v in x.items()}
+    dQ, dK, dV, Ds = masked_attention_grad(sl["q"], sl["k"], sl["v"], g[b:b + 1, :, h:h + 1],
+                                           pred, rows=rows, keys=keys, row_block=256)
+    check("dQ", f64(gq[b:b + 1, rows, h:h + 1]), dQ)
+    check("dK", f64(gk[b:b + 1, keys, h:h + 1]), dK)
+    check("dV", f64(gv[b:b + 1, keys, h:h + 1]), dV)
+    check("D", f64(delta[b:b + 1, h:h + 1, rows]), Ds)
