@@ -124,6 +124,7 @@ def main():
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-primal", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter scaling)")
     args = ap.parse_args()
@@ -203,6 +204,24 @@ def main():
         log(f"primal only: {pms:.3f} ms/call, {pval:.1f} TFLOP/s; JVP/primal time {ms / pms:.2f}")
         res["primal_only"] = {"ms_per_step": round(pms, 4), "tflops": round(pval, 2),
                               "jvp_over_primal_time": round(ms / pms, 3)}
+    if not args.no_backward:
+        # gradients of the primal (dQ, dK, dV) from the forward's O and LSE:
+        # 10*D algorithmic FLOP per admissible pair (S recomputed, dP, dV, dK, dQ)
+        g = torch.randn(xd["q"].shape, generator=torch.Generator().manual_seed(77)).to(
+            xd["q"].dtype).to("cuda")
+        primal()
+        gq, gk, gv = (torch.empty_like(xd["q"]) for _ in range(3))
+        delta = torch.empty_like(lse)
+
+        def backward():
+            aj.attn_jvp_bwd(xd["q"], xd["k"], xd["v"], o, g, lse, mask, g_q=gq, g_k=gk, g_v=gv,
+                            delta=delta, stream=stream)
+
+        bms, _ = time_calls(backward, args.steps, args.warmup, stream)
+        bval = 10 * w.D * pairs * w.B * w.H / (bms * 1e-3) / 1e12
+        log(f"backward: {bms:.3f} ms/call, {bval:.1f} TFLOP/s (10*D FLOP per pair)")
+        res["backward"] = {"ms_per_step": round(bms, 4), "tflops": round(bval, 2),
+                           "flop_per_pair": 10 * w.D}
     traffic = measured_traffic(w.name)
     res["roofline"] = {"bound": "mfma", "achieved": round(value, 2), "peak": PEAK_BF16_TFLOPS,
                        "unit": "TFLOP/s", "frac": round(value / PEAK_BF16_TFLOPS, 4),
