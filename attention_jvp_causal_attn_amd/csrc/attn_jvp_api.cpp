@@ -211,7 +211,7 @@ extern "C" int attn_jvp_bwd(const attn_jvp_bwd_args *a, const attn_jvp_mask *m, 
       !a->delta)
     return ATTN_JVP_ERR_NULL;
   if (a->B <= 0 || a->H <= 0 || a->n_q <= 0 || a->n_k <= 0) return ATTN_JVP_ERR_SHAPE;
-  if (a->dtype != ATTN_JVP_BF16 || a->D != 128) return ATTN_JVP_ERR_UNSUPPORTED;
+  if (a->dtype != ATTN_JVP_BF16 || (a->D != 64 && a->D != 128)) return ATTN_JVP_ERR_UNSUPPORTED;
   if (a->n_q != m->n_q || a->n_k != m->n_k) return ATTN_JVP_ERR_MASK;
   if (!(std::isfinite(a->scale))) return ATTN_JVP_ERR_SHAPE;
   if (int64_t(a->B) * a->H * std::max(a->n_q, a->n_k) > (int64_t(1) << 40)) return ATTN_JVP_ERR_SHAPE;

@@ -1,5 +1,5 @@
 // Gradients of masked attention (the backward of the primal) for gfx950,
-// bf16 in and out, fp32 accumulate, head dim 128.
+// bf16 in and out, fp32 accumulate, head dims 64 and 128.
 //
 // The forward returns the row log-sum-exp so that a backward of the same
 // masked operator can reuse it ("Causal-rCM ..." summary, Appendix B: the
@@ -41,17 +41,23 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int D = 128;
 constexpr int kThreads = 256;
 constexpr int BM = kBwdBlockM;  // rows (or keys) per workgroup
 constexpr int BN = kBwdBlockN;  // keys (or queries) per block
 constexpr int kStages = 3;
-constexpr int KCH = D / 8;      // 16-byte chunks per row
-constexpr int KSTEPS = D / 16;
-constexpr int DT = D / 32;
 constexpr int kEntChunk = 512;
-constexpr int kChunksPerLane = BN * KCH / kThreads;  // per 32 x 128 tensor tile
-static_assert(BM == 128 && BN == 32 && kChunksPerLane * kThreads == BN * KCH, "tile shape");
+static_assert(BM == 128 && BN == 32, "4 waves x 32 rows, 32-row blocks");
+
+// Per head dim: 16-byte chunks per row, k-steps, 32-wide dim tiles, copy
+// chunks per lane per 32-row tensor tile.
+template <int D>
+struct Dims {
+  static constexpr int KCH = D / 8;
+  static constexpr int KSTEPS = D / 16;
+  static constexpr int DT = D / 32;
+  static constexpr int CPL = BN * KCH / kThreads;
+  static_assert(CPL * kThreads == BN * KCH, "whole tiles per copy");
+};
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLog2e = 1.44269504088896340736f;
 
@@ -73,11 +79,17 @@ __device__ __forceinline__ float xor32(float v) { return __shfl_xor(v, 32, 64); 
 __device__ __forceinline__ int swap_bits23(int m) {
   return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
 }
-// 16-byte-chunk XOR swizzle of a 256-byte row, conflict-free both for row
-// reads (16 lanes, 16 rows, one chunk: a bijection of the row's low 4 bits)
-// and for transposed reads (16 lanes, 4 consecutive rows x 32 bytes: the
-// rows land in 4 distinct 32-byte bank windows).
-__device__ __forceinline__ int sw(int row) { return 2 * (row & 7) | ((row >> 3) & 1); }
+// 16-byte-chunk XOR swizzle of a row, conflict-free both for row reads (16
+// lanes read 16 rows at one chunk) and for transposed reads (16 lanes read 4
+// consecutive rows x 32 bytes).  Head dim 128 (256-byte rows): a bijection of
+// the row's low 4 bits whose high 3 bits (the 32-byte window) differ across 4
+// consecutive rows.  Head dim 64 (128-byte rows, two rows per 256-byte bank
+// cycle): a bijection within each row parity whose window bits differ between
+// rows 4a and 4a+2 (and 4a+1, 4a+3).
+template <int D>
+__device__ __forceinline__ int sw(int row) {
+  return D == 128 ? (2 * (row & 7) | ((row >> 3) & 1)) : (2 * ((row >> 1) & 3) | ((row >> 3) & 1));
+}
 
 // 16 bytes per lane straight into LDS at lds_wave + 16 * lane (lds_wave
 // wave-uniform); tracked by vmcnt and waited for explicitly.  One wait state
@@ -105,15 +117,18 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 // Byte offset inside a 32-row block of copy chunk i of this lane (swizzled);
 // rows past the last valid one re-read it (masked out by the schedule).
+template <int D>
 __device__ __forceinline__ uint32_t copy_offset(int i, int64_t row_stride, int rows_valid) {
+  constexpr int KCH = Dims<D>::KCH;
   const int qd = i * kThreads + int(threadIdx.x);
   const int row = qd / KCH, pch = qd % KCH;
   return uint32_t(min(row, rows_valid - 1)) * uint32_t(row_stride) * 2u +
-         uint32_t(pch ^ sw(row)) * 16u;
+         uint32_t(pch ^ sw<D>(row)) * 16u;
 }
 
-// Two 32 x 128 bf16 tiles (rows r0 .. r0+31 of a and b) plus the block's
-// 128 mask words into a stage at LDS st.
+// Two 32 x D bf16 tiles (rows r0 .. r0+31 of a and b) plus the block's 128
+// mask words into a stage at LDS st.
+template <int D>
 __device__ __forceinline__ void copy_pair(uint32_t st, uint32_t a_at, uint32_t b_at,
                                           uint32_t bits_at, int wave, const __bf16 *a,
                                           const __bf16 *b, int64_t row_stride, int r0, int n_rows,
@@ -122,8 +137,8 @@ __device__ __forceinline__ void copy_pair(uint32_t st, uint32_t a_at, uint32_t b
   const int64_t boff = int64_t(r0) * row_stride;
   const int rows = min(BN, n_rows - r0);
 #pragma unroll
-  for (int i = 0; i < kChunksPerLane; ++i) {
-    const uint32_t off = copy_offset(i, row_stride, rows);
+  for (int i = 0; i < Dims<D>::CPL; ++i) {
+    const uint32_t off = copy_offset<D>(i, row_stride, rows);
     const uint32_t chunk = uint32_t(i * kThreads + wave * 64) * 16u;
     dma16(a + boff, off, st + a_at + chunk);
     dma16(b + boff, off, st + b_at + chunk);
@@ -135,20 +150,22 @@ __device__ __forceinline__ void copy_pair(uint32_t st, uint32_t a_at, uint32_t b
 
 // A-operand row read of a swizzled 32 x 128 tile: this lane's row (permuted)
 // at k-step t.
+template <int D>
 __device__ __forceinline__ bf16x8 row_operand(const uint4 *tile, int prow, int t, int hh) {
-  return as_bf16x8(tile[prow * KCH + ((2 * t + hh) ^ sw(prow))]);
+  return as_bf16x8(tile[prow * Dims<D>::KCH + ((2 * t + hh) ^ sw<D>(prow))]);
 }
 
 // A-operand transposed read of a swizzled 32 x 128 tile for step s of 16
 // rows and dim tile nt: within each 16-lane group, lane jl reads row
 // (16s + 4*half + krel) at dims (d0 + 4*(jl%4)) .. +3.
+template <int D>
 __device__ __forceinline__ bf16x8 tr_operand(const uint4 *tile, int s, int nt, int dcol, int krel) {
   bf16x4 h[2];
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     const int row = 16 * s + 4 * half + krel;
     const int d = 32 * nt + dcol;
-    const int chunk = row * KCH + ((d >> 3) ^ sw(row));
+    const int chunk = row * Dims<D>::KCH + ((d >> 3) ^ sw<D>(row));
     const char *ptr = reinterpret_cast<const char *>(tile + chunk) + (d & 7) * 2;
     h[half] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4 *)(ptr));
   }
@@ -165,15 +182,19 @@ __device__ __forceinline__ int reg_pos(int r) {
 
 // ---------------------------------------------------------------- dQ pass
 
+template <int D>
 struct alignas(16) KVTile {
-  uint4 k[BN * KCH];
-  uint4 v[BN * KCH];
+  uint4 k[BN * Dims<D>::KCH];
+  uint4 v[BN * Dims<D>::KCH];
   uint32_t bits[BM];
 };
 
+template <int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_dq_kernel(BwdParams p) {
-  __shared__ KVTile ring[kStages];
+  using Tile = KVTile<D>;
+  constexpr int KSTEPS = Dims<D>::KSTEPS, DT = Dims<D>::DT, CPL = Dims<D>::CPL;
+  __shared__ Tile ring[kStages];
   __shared__ int2 ents[2][kEntChunk];
   const int L = work_item(int(blockIdx.x), p.r_map);
   const int slot = L % p.r_map.n_tiles;
@@ -188,7 +209,7 @@ void bwd_dq_kernel(BwdParams p) {
   const int qrow = tile * BM + row_in_tile;
   const bool qvalid = qrow < p.n_q;
   const uint32_t ring_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&ring[0]));
-  auto stage_lds = [&](int s) { return ring_lds + uint32_t(s) * uint32_t(sizeof(KVTile)); };
+  auto stage_lds = [&](int s) { return ring_lds + uint32_t(s) * uint32_t(sizeof(Tile)); };
 
   const int64_t koff = int64_t(batch) * p.k_sb + int64_t(head) * p.k_sh;
   const __bf16 *kb = static_cast<const __bf16 *>(p.k) + koff;
@@ -210,8 +231,8 @@ void bwd_dq_kernel(BwdParams p) {
   };
   auto bits_of = [&](int2 e) { return p.r_bits + int64_t(e.y >= 0 ? e.y : p.r_partial) * BM; };
   auto issue = [&](int s, int2 e) {
-    copy_pair(stage_lds(s), offsetof(KVTile, k), offsetof(KVTile, v), offsetof(KVTile, bits), wave,
-              kb, vb, p.k_sn, e.x * BN, p.n_k, bits_of(e));
+    copy_pair<D>(stage_lds(s), offsetof(Tile, k), offsetof(Tile, v), offsetof(Tile, bits), wave,
+                 kb, vb, p.k_sn, e.x * BN, p.n_k, bits_of(e));
   };
 
   load_entries(0);
@@ -255,20 +276,20 @@ void bwd_dq_kernel(BwdParams p) {
   for (int j = 0; j < n; ++j) {
     if ((j + 2) % kEntChunk == 0 && j + 2 < n) load_entries((j + 2) / kEntChunk);
     if (j + 1 < n)
-      wait_vmcnt<2 * kChunksPerLane + 1>();
+      wait_vmcnt<2 * CPL + 1>();
     else
       wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     if (j + 2 < n) issue(cur >= 1 ? cur - 1 : cur + 2, entry(j + 2));
-    const KVTile *st = &ring[cur];
+    const Tile *st = &ring[cur];
     const int2 ent = entry(j);
 
     f32x16 S = {}, G = {};
 #pragma unroll
     for (int t = 0; t < KSTEPS; ++t) {
-      S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand(st->k, krow, t, hh), qf[t], S, 0, 0, 0);
-      G = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand(st->v, krow, t, hh), gf[t], G, 0, 0, 0);
+      S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(st->k, krow, t, hh), qf[t], S, 0, 0, 0);
+      G = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(st->v, krow, t, hh), gf[t], G, 0, 0, 0);
     }
     const uint32_t bits = ent.y >= 0 ? st->bits[row_in_tile] >> (8 * hh) : ~0u;
     float gs[16];
@@ -285,7 +306,7 @@ void bwd_dq_kernel(BwdParams p) {
     for (int s = 0; s < 2; ++s) {
 #pragma unroll
       for (int nt = 0; nt < DT; ++nt)
-        acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(st->k, s, nt, dcol, krel),
+        acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(st->k, s, nt, dcol, krel),
                                                           gsb[s], acc[nt], 0, 0, 0);
     }
     cur = cur == kStages - 1 ? 0 : cur + 1;
@@ -308,16 +329,20 @@ void bwd_dq_kernel(BwdParams p) {
 
 // ------------------------------------------------------------ dK/dV pass
 
+template <int D>
 struct alignas(16) QGTile {
-  uint4 q[BN * KCH];
-  uint4 g[BN * KCH];
+  uint4 q[BN * Dims<D>::KCH];
+  uint4 g[BN * Dims<D>::KCH];
   float ld[4 * 16];  // wave w's region: LSE of queries 8w .. 8w+7, then their D
   uint32_t bits[BM];
 };
 
+template <int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_dkv_kernel(BwdParams p) {
-  __shared__ QGTile ring[kStages];
+  using Tile = QGTile<D>;
+  constexpr int KSTEPS = Dims<D>::KSTEPS, DT = Dims<D>::DT, CPL = Dims<D>::CPL;
+  __shared__ Tile ring[kStages];
   __shared__ int2 ents[2][kEntChunk];
   const int L = work_item(int(blockIdx.x), p.c_map);
   const int slot = L % p.c_map.n_tiles;
@@ -332,7 +357,7 @@ void bwd_dkv_kernel(BwdParams p) {
   const int krow_g = tile * BM + key_in_tile;
   const bool kvalid = krow_g < p.n_k;
   const uint32_t ring_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&ring[0]));
-  auto stage_lds = [&](int s) { return ring_lds + uint32_t(s) * uint32_t(sizeof(QGTile)); };
+  auto stage_lds = [&](int s) { return ring_lds + uint32_t(s) * uint32_t(sizeof(Tile)); };
 
   const int64_t qoff = int64_t(batch) * p.q_sb + int64_t(head) * p.q_sh;
   const __bf16 *qb = static_cast<const __bf16 *>(p.q) + qoff;
@@ -355,13 +380,13 @@ void bwd_dkv_kernel(BwdParams p) {
   auto bits_of = [&](int2 e) { return p.c_bits + int64_t(e.y >= 0 ? e.y : p.c_partial) * BM; };
   auto issue = [&](int s, int2 e) {
     const int q0 = e.x * BN;
-    copy_pair(stage_lds(s), offsetof(QGTile, q), offsetof(QGTile, g), offsetof(QGTile, bits), wave,
-              qb, gb, p.q_sn, q0, p.n_q, bits_of(e));
+    copy_pair<D>(stage_lds(s), offsetof(Tile, q), offsetof(Tile, g), offsetof(Tile, bits), wave,
+                 qb, gb, p.q_sn, q0, p.n_q, bits_of(e));
     // LSE and D of queries q0 + 8w .. q0 + 8w + 7 (lanes 0..7, 8..15), clamped
     if (lane < 16) {
       const int qi = min(q0 + 8 * wave + (lane & 7), p.n_q - 1);
       const float *src = lane < 8 ? p.lse + lrow + qi : p.delta + lrow + qi;
-      dma4(src, stage_lds(s) + uint32_t(offsetof(QGTile, ld)) + uint32_t(wave) * 64u);
+      dma4(src, stage_lds(s) + uint32_t(offsetof(Tile, ld)) + uint32_t(wave) * 64u);
     }
   };
 
@@ -401,20 +426,20 @@ void bwd_dkv_kernel(BwdParams p) {
   for (int j = 0; j < n; ++j) {
     if ((j + 2) % kEntChunk == 0 && j + 2 < n) load_entries((j + 2) / kEntChunk);
     if (j + 1 < n)
-      wait_vmcnt<2 * kChunksPerLane + 2>();
+      wait_vmcnt<2 * CPL + 2>();
     else
       wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     if (j + 2 < n) issue(cur >= 1 ? cur - 1 : cur + 2, entry(j + 2));
-    const QGTile *st = &ring[cur];
+    const Tile *st = &ring[cur];
     const int2 ent = entry(j);
 
     f32x16 S = {}, G = {};
 #pragma unroll
     for (int t = 0; t < KSTEPS; ++t) {
-      S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand(st->q, qperm, t, hh), kf[t], S, 0, 0, 0);
-      G = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand(st->g, qperm, t, hh), vf[t], G, 0, 0, 0);
+      S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(st->q, qperm, t, hh), kf[t], S, 0, 0, 0);
+      G = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(st->g, qperm, t, hh), vf[t], G, 0, 0, 0);
     }
     // LSE and D of this lane's 16 queries: 8hh + 0..7 and 16 + 8hh + 0..7
     float lq[16], dq[16];
@@ -449,9 +474,9 @@ void bwd_dkv_kernel(BwdParams p) {
     for (int s = 0; s < 2; ++s) {
 #pragma unroll
       for (int nt = 0; nt < DT; ++nt) {
-        accV[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(st->g, s, nt, dcol, krel),
+        accV[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(st->g, s, nt, dcol, krel),
                                                            pb[s], accV[nt], 0, 0, 0);
-        accK[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(st->q, s, nt, dcol, krel),
+        accK[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(st->q, s, nt, dcol, krel),
                                                            gsb[s], accK[nt], 0, 0, 0);
       }
     }
@@ -479,19 +504,25 @@ void bwd_dkv_kernel(BwdParams p) {
   }
 }
 
-}  // namespace
-
-int launch_bwd_bf16(const BwdParams &p, int D_, void *stream) {
-  if (D_ != D) return hipErrorInvalidValue;
-  hipStream_t s = static_cast<hipStream_t>(stream);
+template <int D>
+hipError_t launch_bwd(const BwdParams &p, hipStream_t s) {
   const int64_t Gq = int64_t(p.r_map.n_tiles) * p.B * p.H;
   const int64_t Gk = int64_t(p.c_map.n_tiles) * p.B * p.H;
   // the dQ pass stores D, which the dK/dV pass reads: same stream, in order
-  hipLaunchKernelGGL(bwd_dq_kernel, dim3(unsigned(Gq)), dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(unsigned(Gq)), dim3(kThreads), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_dkv_kernel, dim3(unsigned(Gk)), dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL(bwd_dkv_kernel<D>, dim3(unsigned(Gk)), dim3(kThreads), 0, s, p);
   return hipGetLastError();
+}
+
+}  // namespace
+
+int launch_bwd_bf16(const BwdParams &p, int D, void *stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (D == 128) return launch_bwd<128>(p, s);
+  if (D == 64) return launch_bwd<64>(p, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace attnjvp

@@ -148,7 +148,7 @@ BAD_BWD = [
     (dict(delta=None), _lib.ATTN_JVP_ERR_NULL),
     (dict(g_v=None), _lib.ATTN_JVP_ERR_NULL),
     (dict(dtype=1), _lib.ATTN_JVP_ERR_UNSUPPORTED),
-    (dict(D=64), _lib.ATTN_JVP_ERR_UNSUPPORTED),
+    (dict(D=96), _lib.ATTN_JVP_ERR_UNSUPPORTED),
     (dict(B=0), _lib.ATTN_JVP_ERR_SHAPE),
     (dict(n_k=11), _lib.ATTN_JVP_ERR_MASK),
     (dict(g_q=0x70008), _lib.ATTN_JVP_ERR_ALIGN),

@@ -65,12 +65,13 @@ SMALL = [
 ]
 
 
+@pytest.mark.parametrize("D", [128, 64])
 @pytest.mark.parametrize("nf,tpf,fpc,B,H", SMALL)
-def test_small_tf_bwd(nf, tpf, fpc, B, H):
-    say(f"case: bwd bf16 TF nf={nf} tpf={tpf} fpc={fpc} B={B} H={H}")
+def test_small_tf_bwd(nf, tpf, fpc, B, H, D):
+    say(f"case: bwd bf16 TF nf={nf} tpf={tpf} fpc={fpc} B={B} H={H} D={D}")
     pred = tf_allowed(nf, tpf, fpc)
-    x = make_random(B, pred.n_q, H, 128, dtype="bf16", seed=9500 + nf * 10 + tpf)
-    g = make_random(B, pred.n_q, H, 128, dtype="bf16", seed=9600 + nf)["q"]
+    x = make_random(B, pred.n_q, H, D, dtype="bf16", seed=9500 + nf * 10 + tpf)
+    g = make_random(B, pred.n_q, H, D, dtype="bf16", seed=9600 + nf)["q"]
     parity(x, g, pred, aj.attn_jvp_mask_tf(nf, tpf, fpc))
 
 
