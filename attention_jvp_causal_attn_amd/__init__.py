@@ -101,6 +101,12 @@ def attn_jvp_mask_rects(n_q, n_k, group_q_begin, range_ptr, k_begin, k_end):
                      kb_p if len(kb) else None, ke_p if len(ke) else None)
 
 
+def attn_jvp_mask_block_causal(n_units, unit_tokens):
+    """Block-causal (diffusion-forcing) mask over one stream (see attn_jvp.h)."""
+    L = _lib.lib()
+    return _new_mask(L.attn_jvp_mask_block_causal, int(n_units), int(unit_tokens))
+
+
 def attn_jvp_mask_dense(n_q, n_k):
     L = _lib.lib()
     return _new_mask(L.attn_jvp_mask_dense, int(n_q), int(n_k))

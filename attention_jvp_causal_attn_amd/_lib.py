@@ -58,6 +58,7 @@ SIGNATURES = {
     "attn_jvp_mask_tf": (_i32, [_i32, _i32, _i32, _PPMASK]),
     "attn_jvp_mask_rects": (_i32, [_i32, _i32, _i32, _pi32, _pi32, _pi32, _pi32, _PPMASK]),
     "attn_jvp_mask_dense": (_i32, [_i32, _i32, _PPMASK]),
+    "attn_jvp_mask_block_causal": (_i32, [_i32, _i32, _PPMASK]),
     "attn_jvp_mask_info": (_i32, [_p, _pi32, _pi32, _pi32, _pi32, _pi64]),
     "attn_jvp_mask_export": (_i32, [_p, _pi32, _pi32, _pi32, _pi32]),
     "attn_jvp_mask_schedule": (_i32, [_p, _i32, _i32, _pi32, _pi64, _pi64, _pi32, _pi32,

@@ -136,6 +136,30 @@ extern "C" int attn_jvp_mask_tf(int32_t n_frames, int32_t tokens_per_frame,
   return ATTN_JVP_OK;
 }
 
+extern "C" int attn_jvp_mask_block_causal(int32_t n_units, int32_t unit_tokens,
+                                          attn_jvp_mask **out) {
+  if (!out) return ATTN_JVP_ERR_NULL;
+  if (n_units <= 0 || unit_tokens <= 0) return ATTN_JVP_ERR_SHAPE;
+  if (int64_t(n_units) * unit_tokens > kMaxTokens) return ATTN_JVP_ERR_SHAPE;
+  const int32_t N = n_units * unit_tokens;
+  std::vector<int32_t> gq;
+  std::vector<std::vector<std::pair<int32_t, int32_t>>> granges;
+  try {
+    for (int u = 0; u < n_units; ++u) {  // unit u: keys of units <= u
+      gq.push_back(u * unit_tokens);
+      granges.push_back({{0, (u + 1) * unit_tokens}});
+    }
+    gq.push_back(N);
+    auto *m = new attn_jvp_mask();
+    m->n_q = m->n_k = N;
+    finish_mask(m, gq, granges);
+    *out = m;
+  } catch (const std::bad_alloc &) {
+    return ATTN_JVP_ERR_OOM;
+  }
+  return ATTN_JVP_OK;
+}
+
 extern "C" int attn_jvp_mask_dense(int32_t n_q, int32_t n_k, attn_jvp_mask **out) {
   const int32_t gq[2] = {0, n_q}, rp[2] = {0, 1}, kb[1] = {0}, ke[1] = {n_k};
   if (!out) return ATTN_JVP_ERR_NULL;

@@ -93,6 +93,15 @@ int attn_jvp_mask_rects(int32_t n_q, int32_t n_k, int32_t n_groups,
                         const int32_t *k_begin, const int32_t *k_end,
                         attn_jvp_mask **out);
 
+/* Block-causal mask over one stream of n_units units of unit_tokens tokens
+ * (N = n_units * unit_tokens): a token of unit u sees every token of units
+ * <= u.  This is the diffusion-forcing layout ("Causal Forcing ..." summary,
+ * Section 2: a noisy frame attends directly to the noisy prefix, with no
+ * clean copy); unit_tokens = 1 gives plain causal attention.
+ * Errors: ERR_NULL, ERR_SHAPE (a size <= 0 or N > 2^30), ERR_OOM. */
+int attn_jvp_mask_block_causal(int32_t n_units, int32_t unit_tokens,
+                               attn_jvp_mask **out);
+
 /* Every query sees every key (plain attention): one group, one range. */
 int attn_jvp_mask_dense(int32_t n_q, int32_t n_k, attn_jvp_mask **out);
 

@@ -11,7 +11,8 @@ import torch
 
 import attention_jvp_causal_attn_amd as aj
 from attention_jvp_causal_attn_amd.inputs import WORKLOADS, make_inputs, make_random
-from oracle import dense_allowed, masked_attention_grad, rects_allowed, tf_allowed
+from oracle import (block_causal_allowed, dense_allowed, masked_attention_grad, rects_allowed,
+                    tf_allowed)
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-2
@@ -100,6 +101,14 @@ def test_dense_bwd():
     x = make_random(2, 300, 2, 128, dtype="bf16", seed=9800)
     g = make_random(2, 300, 2, 128, dtype="bf16", seed=9810)["q"]
     parity(x, g, pred, aj.attn_jvp_mask_dense(300, 300))
+
+
+@pytest.mark.parametrize("D", [128, 64])
+def test_block_causal_bwd(D):
+    pred = block_causal_allowed(6, 70)
+    x = make_random(1, pred.n_q, 2, D, dtype="bf16", seed=9850 + D)
+    g = make_random(1, pred.n_q, 2, D, dtype="bf16", seed=9860 + D)["q"]
+    parity(x, g, pred, aj.attn_jvp_mask_block_causal(6, 70))
 
 
 def test_bwd_deterministic():

@@ -16,8 +16,8 @@ import torch
 
 import attention_jvp_causal_attn_amd as aj
 from attention_jvp_causal_attn_amd.inputs import WORKLOADS, make_inputs, make_random
-from oracle import (dense_allowed, masked_attention, masked_attention_jvp, rects_allowed,
-                    tf_allowed)
+from oracle import (block_causal_allowed, dense_allowed, masked_attention,
+                    masked_attention_jvp, rects_allowed, tf_allowed)
 
 pytestmark = pytest.mark.gpu
 
@@ -353,6 +353,15 @@ def test_absent_tangents_are_zero(dtype, D, given):
     check("O", f64(o1), O, tol)
     check("dO", f64(do1), dO, tol)
     check("LSE", f64(lse1), LSE, tol)
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("bf16", 64), ("f32", 64)])
+def test_block_causal_diffusion_forcing_mask(dtype, D):
+    say(f"case: {dtype} D={D} block-causal 6 x 70")
+    pred = block_causal_allowed(6, 70)
+    x = make_random(1, pred.n_q, 2, D, dtype=dtype, seed=9400 + D, tangent_std=0.1)
+    parity(x, pred, aj.attn_jvp_mask_block_causal(6, 70),
+           TOL[torch.bfloat16 if dtype == "bf16" else torch.float32])
 
 
 def test_strided_views_of_fused_buffers():

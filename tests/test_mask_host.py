@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 
 import attention_jvp_causal_attn_amd as aj
-from oracle import rects_allowed, tf_allowed
+from oracle import block_causal_allowed, rects_allowed, tf_allowed
 
 
 def csr_to_matrix(n_q, n_k, gq, rp, kb, ke):
@@ -273,3 +273,23 @@ def test_rect_transpose_is_matrix_transpose(seed):
     np.testing.assert_array_equal(csr_to_matrix(n_k, n_q, egq, erp, ekb, eke), M.T)
     # the backward's key-tile schedule is the schedule of the transpose
     check_schedule(t, M.T, 128, 32)
+
+
+# ---------------------------------------------------- block-causal (DF) ----
+
+@pytest.mark.parametrize("n_units,unit_tokens", [(1, 1), (5, 1), (4, 37), (21, 13), (3, 130)])
+def test_block_causal_matches_predicate(n_units, unit_tokens):
+    m = aj.attn_jvp_mask_block_causal(n_units, unit_tokens)
+    N = n_units * unit_tokens
+    gq, rp, kb, ke = aj.attn_jvp_mask_export(m)
+    check_canonical(N, N, gq, rp, kb, ke)
+    M = block_causal_allowed(n_units, unit_tokens).matrix()
+    np.testing.assert_array_equal(csr_to_matrix(N, N, gq, rp, kb, ke), M)
+    assert m.info()["n_visible_pairs"] == int(M.sum())
+    check_schedule(m, M, 128, 32)
+
+
+def test_block_causal_errors():
+    for args in [(0, 4), (4, 0), (-1, 3), (1 << 16, 1 << 15)]:
+        with pytest.raises(aj.AttnJvpError):
+            aj.attn_jvp_mask_block_causal(*args)
