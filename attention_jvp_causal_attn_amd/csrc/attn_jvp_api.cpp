@@ -241,7 +241,8 @@ extern "C" int attn_jvp_bwd(const attn_jvp_bwd_args *a, const attn_jvp_mask *m, 
 
   int device = -1;
   if (hipGetDevice(&device) != hipSuccess) return ATTN_JVP_ERR_HIP;
-  const int BM = attnjvp::kBwdBlockM, BN = attnjvp::kBwdBlockN;
+  const int BM = a->D == 128 ? attnjvp::kBwdBlockMWide : attnjvp::kBwdBlockM;
+  const int BN = attnjvp::kBwdBlockN;
   const DeviceSchedule *rs = nullptr, *cs = nullptr;
   const attn_jvp_mask *t = nullptr;
   {
@@ -280,7 +281,8 @@ extern "C" int attn_jvp_bwd(const attn_jvp_bwd_args *a, const attn_jvp_mask *m, 
   p.c_offsets = cs->tile_offsets; p.c_order = cs->tile_order; p.c_entries = cs->entries;
   p.c_bits = cs->partial_bits; p.c_partial = cs->n_partial;
   p.c_map = make_work_map(slices, cs->n_tiles);
-  const int err = attnjvp::launch_bwd_bf16(p, a->D, stream);
+  const int err = a->D == 128 ? attnjvp::launch_bwd_bf16_wide(p, stream)
+                               : attnjvp::launch_bwd_bf16(p, a->D, stream);
   return err == hipSuccess ? ATTN_JVP_OK : ATTN_JVP_ERR_HIP;
 }
 

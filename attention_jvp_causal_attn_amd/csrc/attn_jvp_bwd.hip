@@ -1,5 +1,6 @@
 // Gradients of masked attention (the backward of the primal) for gfx950,
-// bf16 in and out, fp32 accumulate, head dims 64 and 128.
+// bf16 in and out, fp32 accumulate; head dim 64 runs these kernels, head dim
+// 128 the eight-wave versions of attn_jvp_bwd_wide.hip (same formulas).
 //
 // The forward returns the row log-sum-exp so that a backward of the same
 // masked operator can reuse it ("Causal-rCM ..." summary, Appendix B: the

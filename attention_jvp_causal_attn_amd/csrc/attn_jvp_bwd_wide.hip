@@ -1,0 +1,467 @@
+// Backward of masked attention for gfx950, head dim 128: the two passes of
+// attn_jvp_bwd.hip (dQ over query tiles, dK/dV over key tiles of the
+// transposed mask; see there for the formulas) with eight waves per
+// workgroup, two per SIMD, over 256 rows (or keys): one wave's softmax-side
+// vector work runs while the other keeps the matrix core busy.  Every value
+// lives in the 256 VGPRs a wave has at two waves per SIMD; the dK/dV pass
+// therefore stages its V rows in LDS (read as the MFMA B operand) while K
+// stays in registers.  Copies go through a 2-stage ring: block j + 1 is
+// copied while block j is computed.
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+
+#include "internal.h"
+
+namespace attnjvp {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int D = 128;
+constexpr int kThreads = 512;
+constexpr int BM = kBwdBlockMWide;  // 256 rows (or keys) per workgroup
+constexpr int BN = kBwdBlockN;      // 32 keys (or queries) per block
+constexpr int KCH = D / 8;
+constexpr int KSTEPS = D / 16;
+constexpr int DT = D / 32;
+constexpr int kEntChunk = 512;
+static_assert(BM == 256 && BN == 32 && BN * KCH == kThreads, "one chunk per lane per tile");
+constexpr float kLog2e = 1.44269504088896340736f;
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 x) { return __builtin_bit_cast(bf16x8, x); }
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+__device__ __forceinline__ bf16x8 to_bf16x8(const float *x) {
+  const f32x8 v = {x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]};
+  return __builtin_convertvector(v, bf16x8);
+}
+__device__ __forceinline__ float xor32(float v) { return __shfl_xor(v, 32, 64); }
+// Bits 2 and 3 of a 32-row tile index swapped (see attn_jvp_bwd.hip).
+__device__ __forceinline__ int swap_bits23(int m) {
+  return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
+}
+// Chunk swizzle of 256-byte rows, conflict-free for row and transposed reads
+// (see attn_jvp_bwd.hip).
+__device__ __forceinline__ int sw(int row) { return 2 * (row & 7) | ((row >> 3) & 1); }
+
+// 16 bytes per lane straight into LDS at lds_wave + 16 * lane (lds_wave
+// wave-uniform); tracked by vmcnt and waited for explicitly.  One wait state
+// separates the M0 write from the copy.
+__device__ __forceinline__ void dma16(const void *base, uint32_t voff, uint32_t lds_wave) {
+  lds_wave = __builtin_amdgcn_readfirstlane(lds_wave);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(base), "s"(lds_wave)
+               : "memory", "m0");
+}
+// 4 bytes per lane from a per-lane address into LDS at lds_wave + 4 * lane.
+__device__ __forceinline__ void dma4(const void *addr, uint32_t lds_wave) {
+  lds_wave = __builtin_amdgcn_readfirstlane(lds_wave);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :
+               : "v"(addr), "s"(lds_wave)
+               : "memory", "m0");
+}
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// This lane's copy chunk of a 32-row block (swizzled); rows past the last
+// valid one re-read it (masked out by the schedule).
+__device__ __forceinline__ uint32_t copy_offset(int64_t row_stride, int rows_valid) {
+  const int q = int(threadIdx.x);
+  const int row = q / KCH, pch = q % KCH;
+  return uint32_t(min(row, rows_valid - 1)) * uint32_t(row_stride) * 2u +
+         uint32_t(pch ^ sw(row)) * 16u;
+}
+
+// Two 32 x 128 tiles (rows r0 .. r0+31 of a and b) and the block's 256 mask
+// words into a stage.
+__device__ __forceinline__ void copy_pair(uint32_t st, uint32_t a_at, uint32_t b_at,
+                                          uint32_t bits_at, int wave, const __bf16 *a,
+                                          const __bf16 *b, int64_t row_stride, int r0, int n_rows,
+                                          const uint32_t *bits_src) {
+  const int lane = threadIdx.x & 63;
+  const int64_t boff = int64_t(r0) * row_stride;
+  const uint32_t off = copy_offset(row_stride, min(BN, n_rows - r0));
+  const uint32_t chunk = uint32_t(wave * 64) * 16u;
+  dma16(a + boff, off, st + a_at + chunk);
+  dma16(b + boff, off, st + b_at + chunk);
+  // mask bits: BM words = 64 chunks; wave w copies chunks 8w .. 8w+7 (lanes 0..7)
+  if (lane < 8)
+    dma16(bits_src, uint32_t(wave * 8 + lane) * 16u, st + bits_at + uint32_t(wave) * 128u);
+}
+
+__device__ __forceinline__ bf16x8 row_operand(const uint4 *tile, int prow, int t, int hh) {
+  return as_bf16x8(tile[prow * KCH + ((2 * t + hh) ^ sw(prow))]);
+}
+__device__ __forceinline__ bf16x8 tr_operand(const uint4 *tile, int s, int nt, int dcol, int krel) {
+  bf16x4 h[2];
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int row = 16 * s + 4 * half + krel;
+    const int d = 32 * nt + dcol;
+    const int chunk = row * KCH + ((d >> 3) ^ sw(row));
+    const char *ptr = reinterpret_cast<const char *>(tile + chunk) + (d & 7) * 2;
+    h[half] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4 *)(ptr));
+  }
+  return __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ int reg_pos(int r) {
+  const int j = r >> 2, i = r & 3;
+  return 16 * (j >> 1) + 4 * (j & 1) + i;
+}
+
+// Per-lane constants of the transposed reads, opaque so that they are
+// rebuilt per block rather than held across the key loop.
+struct TrLane {
+  int dcol, krel;
+};
+__device__ __forceinline__ TrLane tr_lane() {
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4, jl = lane & 15;
+  int dcol = 16 * (g & 1) + 4 * (jl & 3);
+  int krel = 8 * (lane >> 5) + (jl >> 2);
+  asm volatile("" : "+v"(dcol), "+v"(krel));
+  return {dcol, krel};
+}
+
+// ---------------------------------------------------------------- dQ pass
+
+struct alignas(16) KVTile {
+  uint4 k[BN * KCH];
+  uint4 v[BN * KCH];
+  uint32_t bits[BM];
+};
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dq_wide_kernel(BwdParams p) {
+  __shared__ KVTile ring[2];
+  __shared__ int2 ents[2][kEntChunk];
+  const int L = work_item(int(blockIdx.x), p.r_map);
+  const int slot = L % p.r_map.n_tiles;
+  const int bh = L / p.r_map.n_tiles;
+  const int head = bh % p.H, batch = bh / p.H;
+  const int tile = p.r_order[slot];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 31, hh = lane >> 5;
+  const int row_in_tile = wave * 32 + col;
+  const int qrow = tile * BM + row_in_tile;
+  const bool qvalid = qrow < p.n_q;
+  const uint32_t ring_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&ring[0]));
+  auto stage_lds = [&](int s) { return ring_lds + uint32_t(s) * uint32_t(sizeof(KVTile)); };
+
+  const int64_t koff = int64_t(batch) * p.k_sb + int64_t(head) * p.k_sh;
+  const __bf16 *kb = static_cast<const __bf16 *>(p.k) + koff;
+  const __bf16 *vb = static_cast<const __bf16 *>(p.v) + koff;
+  const int64_t qoff = int64_t(batch) * p.q_sb + int64_t(head) * p.q_sh;
+  const int64_t lrow = (int64_t(batch) * p.H + head) * p.n_q;
+
+  const int e0 = p.r_offsets[tile], e1 = p.r_offsets[tile + 1];
+  const int n = e1 - e0;
+  auto load_entries = [&](int c) {
+    int2 *dst = ents[c & 1];
+    const int base = e0 + c * kEntChunk;
+    for (int i = threadIdx.x; i < kEntChunk; i += kThreads)
+      dst[i] = base + i < e1 ? p.r_entries[base + i] : make_int2(0, -1);
+  };
+  auto entry = [&](int j) {
+    const int2 e = ents[(j / kEntChunk) & 1][j % kEntChunk];
+    return make_int2(__builtin_amdgcn_readfirstlane(e.x), __builtin_amdgcn_readfirstlane(e.y));
+  };
+  auto bits_of = [&](int2 e) { return p.r_bits + int64_t(e.y >= 0 ? e.y : p.r_partial) * BM; };
+  auto issue = [&](int s, int2 e) {
+    copy_pair(stage_lds(s), offsetof(KVTile, k), offsetof(KVTile, v), offsetof(KVTile, bits), wave,
+              kb, vb, p.k_sn, e.x * BN, p.n_k, bits_of(e));
+  };
+
+  load_entries(0);
+  __syncthreads();
+  if (n > 0) issue(0, entry(0));
+
+  bf16x8 qf[KSTEPS], gf[KSTEPS];
+  float dsum = 0.f;
+  {
+    const int qr = qvalid ? qrow : 0;
+    const int64_t off = qoff + int64_t(qr) * p.q_sn + 8 * hh;
+    const __bf16 *qb = static_cast<const __bf16 *>(p.q) + off;
+    const __bf16 *gb = static_cast<const __bf16 *>(p.g_o) + off;
+    const __bf16 *ob = static_cast<const __bf16 *>(p.o) + off;
+#pragma unroll
+    for (int t = 0; t < KSTEPS; ++t) {
+      qf[t] = as_bf16x8(*reinterpret_cast<const uint4 *>(qb + 16 * t));
+      gf[t] = as_bf16x8(*reinterpret_cast<const uint4 *>(gb + 16 * t));
+      const bf16x8 of = as_bf16x8(*reinterpret_cast<const uint4 *>(ob + 16 * t));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dsum = __builtin_fmaf(float(gf[t][e]), float(of[e]), dsum);
+    }
+  }
+  dsum += xor32(dsum);
+  const float lse2 = qvalid ? p.lse[lrow + qrow] * kLog2e : 0.f;
+  if (qvalid && hh == 0) p.delta[lrow + qrow] = dsum;
+
+  f32x16 acc[DT];
+#pragma unroll
+  for (int nt = 0; nt < DT; ++nt) acc[nt] = f32x16{};
+  const float sl2 = p.scale_log2;
+
+  for (int j = 0; j < n; ++j) {
+    if ((j + 1) % kEntChunk == 0 && j + 1 < n) load_entries((j + 1) / kEntChunk);
+    wait_vmcnt<0>();  // block j (and, first time, Q, g, O) has landed
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    const KVTile *st = &ring[j & 1];
+    const int2 ent = entry(j);
+    int krow = swap_bits23(col);
+    asm volatile("" : "+v"(krow));
+    f32x16 S = {}, G = {};
+#pragma unroll
+    for (int t = 0; t < KSTEPS; ++t) {
+      S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand(st->k, krow, t, hh), qf[t], S, 0, 0, 0);
+      G = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand(st->v, krow, t, hh), gf[t], G, 0, 0, 0);
+      if (t % 2 == 1) __builtin_amdgcn_sched_barrier(0);  // bound the operand prefetch
+    }
+    if (j + 1 < n) issue((j + 1) & 1, entry(j + 1));  // its stage was released by the barrier
+    const uint32_t bits = ent.y >= 0 ? st->bits[row_in_tile] >> (8 * hh) : ~0u;
+    float gs[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const bool ok = (bits >> reg_pos(r)) & 1u;
+      const float pr = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], sl2, -lse2)) : 0.f;
+      gs[r] = pr * (G[r] - dsum);
+    }
+    bf16x8 gsb[2];
+    gsb[0] = to_bf16x8(gs);
+    gsb[1] = to_bf16x8(gs + 8);
+    const TrLane tl = tr_lane();
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+#pragma unroll
+      for (int nt = 0; nt < DT; ++nt) {
+        acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(st->k, s, nt, tl.dcol, tl.krel),
+                                                          gsb[s], acc[nt], 0, 0, 0);
+        if (nt % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+  wait_vmcnt<0>();
+
+  if (!qvalid) return;
+  __bf16 *out = static_cast<__bf16 *>(p.g_q) + qoff + int64_t(qrow) * p.q_sn;
+#pragma unroll
+  for (int nt = 0; nt < DT; ++nt) {
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int d0 = 32 * nt + 8 * jj + 4 * hh;
+      float x[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = acc[nt][4 * jj + i] * p.scale;
+      *reinterpret_cast<uint2 *>(out + d0) = make_uint2(pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]));
+    }
+  }
+}
+
+// ------------------------------------------------------------ dK/dV pass
+
+struct alignas(16) QGTile {
+  uint4 q[BN * KCH];
+  uint4 g[BN * KCH];
+  float ld[8 * 8];  // wave w's region: LSE of queries 4w .. 4w+3, then their D
+  uint32_t bits[BM];
+};
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dkv_wide_kernel(BwdParams p) {
+  __shared__ QGTile ring[2];
+  __shared__ uint4 v_lds[BM * KCH];  // this tile's V rows (B operands), 64 KB
+  __shared__ int2 ents[2][kEntChunk];
+  const int L = work_item(int(blockIdx.x), p.c_map);
+  const int slot = L % p.c_map.n_tiles;
+  const int bh = L / p.c_map.n_tiles;
+  const int head = bh % p.H, batch = bh / p.H;
+  const int tile = p.c_order[slot];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 31, hh = lane >> 5;
+  const int key_in_tile = wave * 32 + col;
+  const int krow_g = tile * BM + key_in_tile;
+  const bool kvalid = krow_g < p.n_k;
+  const uint32_t ring_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&ring[0]));
+  auto stage_lds = [&](int s) { return ring_lds + uint32_t(s) * uint32_t(sizeof(QGTile)); };
+
+  const int64_t qoff = int64_t(batch) * p.q_sb + int64_t(head) * p.q_sh;
+  const __bf16 *qb = static_cast<const __bf16 *>(p.q) + qoff;
+  const __bf16 *gb = static_cast<const __bf16 *>(p.g_o) + qoff;
+  const int64_t koff = int64_t(batch) * p.k_sb + int64_t(head) * p.k_sh;
+  const int64_t lrow = (int64_t(batch) * p.H + head) * p.n_q;
+
+  const int e0 = p.c_offsets[tile], e1 = p.c_offsets[tile + 1];
+  const int n = e1 - e0;
+  auto load_entries = [&](int c) {
+    int2 *dst = ents[c & 1];
+    const int base = e0 + c * kEntChunk;
+    for (int i = threadIdx.x; i < kEntChunk; i += kThreads)
+      dst[i] = base + i < e1 ? p.c_entries[base + i] : make_int2(0, -1);
+  };
+  auto entry = [&](int j) {
+    const int2 e = ents[(j / kEntChunk) & 1][j % kEntChunk];
+    return make_int2(__builtin_amdgcn_readfirstlane(e.x), __builtin_amdgcn_readfirstlane(e.y));
+  };
+  auto bits_of = [&](int2 e) { return p.c_bits + int64_t(e.y >= 0 ? e.y : p.c_partial) * BM; };
+  auto issue = [&](int s, int2 e) {
+    const int q0 = e.x * BN;
+    copy_pair(stage_lds(s), offsetof(QGTile, q), offsetof(QGTile, g), offsetof(QGTile, bits), wave,
+              qb, gb, p.q_sn, q0, p.n_q, bits_of(e));
+    // LSE and D of queries q0 + 4w .. q0 + 4w + 3 (lanes 0..3, 4..7), clamped
+    if (lane < 8) {
+      const int qi = min(q0 + 4 * wave + (lane & 3), p.n_q - 1);
+      const float *src = lane < 4 ? p.lse + lrow + qi : p.delta + lrow + qi;
+      dma4(src, stage_lds(s) + uint32_t(offsetof(QGTile, ld)) + uint32_t(wave) * 32u);
+    }
+  };
+
+  load_entries(0);
+  __syncthreads();
+  if (n > 0) issue(0, entry(0));
+  // V rows of the tile -> LDS (rows past n_k re-read the last key), K -> registers
+  {
+    const uint32_t v_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&v_lds[0]));
+    const __bf16 *vb = static_cast<const __bf16 *>(p.v) + koff;
+#pragma unroll
+    for (int i = 0; i < BM * KCH / kThreads; ++i) {
+      const int q = i * kThreads + threadIdx.x;
+      const int row = q / KCH, pch = q % KCH;
+      const int grow = min(tile * BM + row, p.n_k - 1);
+      dma16(vb, uint32_t(grow) * uint32_t(p.k_sn) * 2u + uint32_t(pch ^ sw(row)) * 16u,
+            v_base + uint32_t(i * kThreads + wave * 64) * 16u);
+    }
+  }
+  bf16x8 kf[KSTEPS];
+  {
+    const int kr = kvalid ? krow_g : 0;
+    const __bf16 *kp = static_cast<const __bf16 *>(p.k) + koff + int64_t(kr) * p.k_sn + 8 * hh;
+#pragma unroll
+    for (int t = 0; t < KSTEPS; ++t) kf[t] = as_bf16x8(*reinterpret_cast<const uint4 *>(kp + 16 * t));
+  }
+
+  f32x16 accK[DT], accV[DT];
+#pragma unroll
+  for (int nt = 0; nt < DT; ++nt) {
+    accK[nt] = f32x16{};
+    accV[nt] = f32x16{};
+  }
+  const float sl2 = p.scale_log2;
+
+  for (int j = 0; j < n; ++j) {
+    if ((j + 1) % kEntChunk == 0 && j + 1 < n) load_entries((j + 1) / kEntChunk);
+    wait_vmcnt<0>();  // block j (and, first time, V and K) has landed
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    const QGTile *st = &ring[j & 1];
+    const int2 ent = entry(j);
+    int qperm = swap_bits23(col);
+    asm volatile("" : "+v"(qperm));
+    const uint4 *vrow = v_lds + key_in_tile * KCH;
+    f32x16 S = {}, G = {};
+#pragma unroll
+    for (int t = 0; t < KSTEPS; ++t) {
+      const bf16x8 vf = as_bf16x8(vrow[(2 * t + hh) ^ sw(key_in_tile)]);
+      S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand(st->q, qperm, t, hh), kf[t], S, 0, 0, 0);
+      G = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand(st->g, qperm, t, hh), vf, G, 0, 0, 0);
+      if (t % 2 == 1) __builtin_amdgcn_sched_barrier(0);  // bound the operand prefetch
+    }
+    if (j + 1 < n) issue((j + 1) & 1, entry(j + 1));  // its stage was released by the barrier
+    // LSE and D of this lane's 16 queries 8hh + {0..7} and 16 + 8hh + {0..7}:
+    // query q sits in region q / 4 at slot q % 4 (LSE) and 4 + q % 4 (D)
+    float lq[16], dq[16];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+      for (int rg = 0; rg < 2; ++rg) {
+        const float4 *reg = reinterpret_cast<const float4 *>(st->ld + 8 * (4 * half + 2 * hh + rg));
+        const float4 a = reg[0], b = reg[1];
+        lq[8 * half + 4 * rg + 0] = a.x; lq[8 * half + 4 * rg + 1] = a.y;
+        lq[8 * half + 4 * rg + 2] = a.z; lq[8 * half + 4 * rg + 3] = a.w;
+        dq[8 * half + 4 * rg + 0] = b.x; dq[8 * half + 4 * rg + 1] = b.y;
+        dq[8 * half + 4 * rg + 2] = b.z; dq[8 * half + 4 * rg + 3] = b.w;
+      }
+    }
+    const uint32_t bits = ent.y >= 0 ? st->bits[key_in_tile] >> (8 * hh) : ~0u;
+    float pr[16], gs[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int pos = reg_pos(r);
+      const int e = 8 * (pos >> 4) + (pos & 7);
+      const bool ok = (bits >> pos) & 1u;
+      pr[r] = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], sl2, -lq[e] * kLog2e)) : 0.f;
+      gs[r] = pr[r] * (G[r] - dq[e]);
+    }
+    bf16x8 pb[2], gsb[2];
+    pb[0] = to_bf16x8(pr);
+    pb[1] = to_bf16x8(pr + 8);
+    gsb[0] = to_bf16x8(gs);
+    gsb[1] = to_bf16x8(gs + 8);
+    const TrLane tl = tr_lane();
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+#pragma unroll
+      for (int nt = 0; nt < DT; ++nt) {
+        accV[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(st->g, s, nt, tl.dcol, tl.krel),
+                                                           pb[s], accV[nt], 0, 0, 0);
+        accK[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(st->q, s, nt, tl.dcol, tl.krel),
+                                                           gsb[s], accK[nt], 0, 0, 0);
+        if (nt % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+  wait_vmcnt<0>();
+
+  if (!kvalid) return;
+  const int64_t ooff = koff + int64_t(krow_g) * p.k_sn;
+  __bf16 *gk = static_cast<__bf16 *>(p.g_k) + ooff;
+  __bf16 *gv = static_cast<__bf16 *>(p.g_v) + ooff;
+#pragma unroll
+  for (int nt = 0; nt < DT; ++nt) {
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int d0 = 32 * nt + 8 * jj + 4 * hh;
+      float xk[4], xv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        xk[i] = accK[nt][4 * jj + i] * p.scale;
+        xv[i] = accV[nt][4 * jj + i];
+      }
+      *reinterpret_cast<uint2 *>(gk + d0) = make_uint2(pack_bf16(xk[0], xk[1]), pack_bf16(xk[2], xk[3]));
+      *reinterpret_cast<uint2 *>(gv + d0) = make_uint2(pack_bf16(xv[0], xv[1]), pack_bf16(xv[2], xv[3]));
+    }
+  }
+}
+
+}  // namespace
+
+int launch_bwd_bf16_wide(const BwdParams &p, void *stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t Gq = int64_t(p.r_map.n_tiles) * p.B * p.H;
+  const int64_t Gk = int64_t(p.c_map.n_tiles) * p.B * p.H;
+  // the dQ pass stores D, which the dK/dV pass reads: same stream, in order
+  hipLaunchKernelGGL(bwd_dq_wide_kernel, dim3(unsigned(Gq)), dim3(kThreads), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_dkv_wide_kernel, dim3(unsigned(Gk)), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace attnjvp

@@ -151,13 +151,15 @@ const HostSchedule *host_schedule_locked(const attn_jvp_mask *m, int block_m,
 int launch_bf16(const KernelParams &p, int D, bool tangent, void *stream);
 int launch_bf16_wide(const KernelParams &p, bool tangent, void *stream);  // D = 128
 int launch_bwd_bf16(const BwdParams &p, int D, void *stream);
+int launch_bwd_bf16_wide(const BwdParams &p, void *stream);  // D = 128
 int launch_f32(const KernelParams &p, int D, bool tangent, void *stream);
 
 // Tile shapes of the kernels.
 constexpr int kBf16BlockM = 128;      // head dim 64: 4 waves x 32 rows
 constexpr int kBf16BlockMWide = 256;  // head dim 128: 8 waves x 32 rows
 constexpr int kBf16BlockN = 32;
-constexpr int kBwdBlockM = 128;       // backward: 4 waves x 32 rows (or keys)
+constexpr int kBwdBlockM = 128;       // backward, head dim 64: 4 waves x 32 rows (or keys)
+constexpr int kBwdBlockMWide = 256;   // backward, head dim 128: 8 waves x 32 rows (or keys)
 constexpr int kBwdBlockN = 32;        // backward: blocks of 32 keys (or queries)
 constexpr int kF32BlockM = 64;
 constexpr int kF32BlockN = 32;
