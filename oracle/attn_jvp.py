@@ -21,7 +21,12 @@ For one (batch b, head h) slice and query row i, with J_i the admissible keys,
     dO_i  = sum_j p_j (ds_j - mu_i) v_j + sum_j p_j dv_j
 
 The last line is the product rule applied to O_i = sum_j p_j v_j with
-dp_j = p_j (ds_j - mu_i), the derivative of the normalised softmax.
+dp_j = p_j (ds_j - mu_i), the derivative of the normalised softmax.  The
+tangent of the row log-sum-exp (returned on request: the appendix lists LSE
+among the outputs, and its derivative is the softmax-weighted mean of the
+score tangents) is
+
+    dLSE_i = mu_i = sum_j p_j ds_j
 ``scale`` defaults to 1/sqrt(D) and carries no tangent (the pages are silent
 on the scale; the usual attention default is taken).  A row with no admissible
 key gets O = 0, dO = 0 and LSE = -inf (the pages are silent; TF masks never
@@ -53,14 +58,15 @@ def _prep(q, scale, rows, n):
 
 
 def masked_attention_jvp(q, k, v, dq, dk, dv, allowed, scale=None, rows=None,
-                         row_block=512):
+                         row_block=512, lse_tangent=False):
     """Masked attention and its tangent.
 
     q, k, v, dq, dk, dv : array-like [B, N, H, D] (numpy or torch, any float
                           dtype); one (b, h) slice at a time is widened to fp64
     allowed : predicate object, ``allowed(rows) -> bool [len(rows), N]``
     rows    : query rows to evaluate (default: all N)
-    returns (O, dO, LSE) as fp64: O, dO [B, R, H, D], LSE [B, H, R]
+    returns (O, dO, LSE) as fp64: O, dO [B, R, H, D], LSE [B, H, R]; with
+    ``lse_tangent`` also dLSE [B, H, R] (0 for rows without keys)
     """
     B, N, H, D = q.shape
     scale, rows = _prep(q, scale, rows, N)
@@ -68,6 +74,7 @@ def masked_attention_jvp(q, k, v, dq, dk, dv, allowed, scale=None, rows=None,
     O = np.zeros((B, R, H, D))
     dO = np.zeros((B, R, H, D))
     LSE = np.full((B, H, R), -np.inf)
+    dLSE = np.zeros((B, H, R))
     blocks = []
     for r0 in range(0, R, row_block):
         rb = rows[r0:r0 + row_block]
@@ -96,6 +103,9 @@ def masked_attention_jvp(q, k, v, dq, dk, dv, allowed, scale=None, rows=None,
                 dO[b, r0:r0 + len(rb), h, :] = dp @ vj + p @ dvj
                 lse = np.where(live, m[:, 0] + np.log(np.where(live, l[:, 0], 1.0)), -np.inf)
                 LSE[b, h, r0:r0 + len(rb)] = lse
+                dLSE[b, h, r0:r0 + len(rb)] = mu[:, 0]
+    if lse_tangent:
+        return O, dO, LSE, dLSE
     return O, dO, LSE
 
 

@@ -183,6 +183,38 @@ def test_tangent_central_finite_difference(mname, D):
     assert rel <= 1e-7, rel
 
 
+@pytest.mark.parametrize("mname,D", [("tf_frame", 4), ("tf_chunk", 16), ("rects", 16)])
+def test_lse_tangent_central_finite_difference(mname, D):
+    pred = MASKS[mname]()
+    x = _six(1, pred.n_q, 2, D, seed=33)
+    eps = 1e-6
+    plus = [a + eps * b for a, b in zip(x[:3], x[3:])]
+    minus = [a - eps * b for a, b in zip(x[:3], x[3:])]
+    _, Lp = masked_attention(*plus, pred)
+    _, Lm = masked_attention(*minus, pred)
+    live = np.isfinite(Lp)
+    fd = np.where(live, (Lp - Lm) / (2 * eps), 0.0)
+    *_, dL = masked_attention_jvp(*x, pred, lse_tangent=True)
+    rel = np.abs(dL - fd).max() / np.abs(fd).max()
+    assert rel <= 1e-7, rel
+
+
+def test_lse_tangent_matches_torch_forward_ad():
+    pred = MASKS["tf_chunk"]()
+    q, k, v, dq, dk, dv = _six(1, pred.n_q, 2, 8, seed=35, tstd=0.3)
+    M = torch.from_numpy(pred.matrix())
+    sc = 1 / math.sqrt(8)
+
+    def lse(q_, k_):
+        S = (q_ @ k_.transpose(-1, -2)) * sc
+        return torch.logsumexp(S.masked_fill(~M, float("-inf")), dim=-1)
+
+    t = lambda x: torch.from_numpy(x).permute(0, 2, 1, 3)
+    _, ref = jvp(lse, (t(q), t(k)), (t(dq), t(dk)))
+    *_, dL = masked_attention_jvp(q, k, v, dq, dk, dv, pred, lse_tangent=True)
+    np.testing.assert_allclose(dL, ref.numpy(), rtol=1e-11, atol=1e-13)
+
+
 # ------------------------------------------------------- closed forms ----
 
 def test_zero_query_key_tangents_gives_p_dv():
@@ -229,6 +261,26 @@ def test_zero_queries_give_uniform_weights():
         np.testing.assert_allclose(O[0, :, h], (M @ v[0, :, h]) / cnt[:, None], rtol=1e-13)
         np.testing.assert_allclose(dO[0, :, h], (M @ dv[0, :, h]) / cnt[:, None], rtol=1e-12, atol=1e-14)
         np.testing.assert_allclose(LSE[0, h], np.log(cnt), rtol=1e-14)
+
+
+def test_lse_tangent_closed_forms():
+    pred = tf_allowed(3, 4, 1)
+    q, k, v, dq, dk, dv = _six(1, pred.n_q, 2, 8, seed=63)
+    z = np.zeros_like(q)
+    # only dV moves: the scores, hence LSE, do not
+    *_, dL = masked_attention_jvp(q, k, v, z, z, dv, pred, lse_tangent=True)
+    assert np.all(dL == 0)
+    # q = 0: uniform weights, dLSE = mean over J of scale <dq, k_j>
+    *_, dL = masked_attention_jvp(z, k, v, dq, z, dv, pred, lse_tangent=True)
+    M = pred.matrix()
+    sc = 1 / math.sqrt(8)
+    for h in range(2):
+        ds = sc * (dq[0, :, h] @ k[0, :, h].T)
+        np.testing.assert_allclose(dL[0, h], (M * ds).sum(1) / M.sum(1), rtol=1e-12, atol=1e-14)
+    # a row without keys has dLSE = 0
+    pr = rects_allowed(4, 4, [(0, 2, 0, 4)])
+    *_, dL = masked_attention_jvp(*_six(1, 4, 1, 4, seed=64), pr, lse_tangent=True)
+    assert np.all(dL[0, 0, 2:] == 0) and np.all(dL[0, 0, :2] != 0)
 
 
 def test_zero_queries_covariance_form():
