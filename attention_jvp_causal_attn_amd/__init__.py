@@ -19,7 +19,9 @@ from ._lib import ATTN_JVP_BF16, ATTN_JVP_F32  # noqa: F401
 __all__ = [
     "AttnJvpError", "Mask", "attn_jvp_mask_tf", "attn_jvp_mask_rects", "attn_jvp_mask_dense",
     "attn_jvp_mask_info", "attn_jvp_mask_export", "attn_jvp_mask_schedule", "attn_jvp_mask_free",
-    "attn_jvp_fwd", "attn_jvp_tile_shape", "attn_jvp_status_str", "attn_jvp_version",
+    "attn_jvp_mask_block_causal", "attn_jvp_mask_transpose", "attn_jvp_mask_split_schedule",
+    "attn_jvp_fwd", "attn_jvp_fwd_split_workspace", "attn_jvp_split_choose", "attn_jvp_bwd", "attn_jvp_tile_shape",
+    "attn_jvp_status_str", "attn_jvp_version",
 ]
 
 
@@ -188,15 +190,23 @@ def _dtype_code(t):
 
 
 def attn_jvp_fwd(q, k, v, dq, dk, dv, mask, scale=None, o=None, d_o=None, lse=None,
-                 stream=None):
+                 stream=None, lse_tangent=False, d_lse=None, max_splits=1, workspace=None):
     """Masked attention O, its tangent dO and the row log-sum-exp, in one pass.
 
     q, dq: [B, n_q, H, D]; k, v, dk, dv: [B, n_k, H, D] device tensors of one
     dtype (bfloat16 or float32), last dim contiguous; q-side tensors (q, dq
-    and the outputs o, d_o) share strides, as do the k-side ones.  Pass
-    dq = dk = dv = None for the primal only (then d_o is None).  Outputs are
-    allocated when not given.  The call is asynchronous on ``stream`` (default:
-    torch's current stream).  Returns (o, d_o, lse) with lse [B, H, n_q] fp32.
+    and the outputs o, d_o) share strides, as do the k-side ones.  Any tangent
+    may be None (zero); all three None gives the primal only (then d_o is
+    None).  Outputs are allocated when not given.  The call is asynchronous on
+    ``stream`` (default: torch's current stream).  Returns (o, d_o, lse) with
+    lse [B, H, n_q] fp32, and d_lse (the tangent of lse, same shape) as a
+    fourth element when ``lse_tangent`` is set or ``d_lse`` is given.
+
+    max_splits > 1 selects the split-key launch (attn_jvp_fwd_split): long
+    key lists are cut into up to max_splits pieces run in parallel and merged;
+    its scratch ``workspace`` (a uint8 device tensor) is allocated when not
+    given.  max_splits="auto" lets attn_jvp_split_choose pick the count for
+    this device.
     """
     import torch
     tangent = dq is not None or dk is not None or dv is not None
@@ -215,12 +225,17 @@ def attn_jvp_fwd(q, k, v, dq, dk, dv, mask, scale=None, o=None, d_o=None, lse=No
     if not q.is_cuda:
         raise ValueError("tensors must live on the GPU")
     code = _dtype_code(q)
+    want_dlse = lse_tangent or d_lse is not None
+    if want_dlse and not tangent:
+        raise ValueError("the tangent of lse needs at least one input tangent")
     if o is None:
         o = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
     if tangent and d_o is None:
         d_o = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
     if lse is None:
         lse = torch.empty((B, H, n_q), dtype=torch.float32, device=q.device)
+    if want_dlse and d_lse is None:
+        d_lse = torch.empty((B, H, n_q), dtype=torch.float32, device=q.device)
     for name, t in (("dq", dq), ("o", o), ("d_o", d_o)):
         if t is not None and (tuple(t.shape) != tuple(q.shape) or t.stride() != q.stride()
                               or t.dtype != q.dtype):
@@ -230,8 +245,10 @@ def attn_jvp_fwd(q, k, v, dq, dk, dv, mask, scale=None, o=None, d_o=None, lse=No
             raise ValueError(f"{name} must have the strides of k")
     if q.stride(3) != 1 or k.stride(3) != 1:
         raise ValueError("the last dimension must be contiguous")
-    if tuple(lse.shape) != (B, H, n_q) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 [B, H, n_q] tensor")
+    for name, t in (("lse", lse), ("d_lse", d_lse)):
+        if t is not None and (tuple(t.shape) != (B, H, n_q) or t.dtype != torch.float32
+                              or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous float32 [B, H, n_q] tensor")
     ptr = lambda t: t.data_ptr() if t is not None else None
     a = _lib.AttnJvpArgs(
         dtype=code, B=B, H=H, n_q=n_q, n_k=n_k, D=D,
@@ -239,14 +256,101 @@ def attn_jvp_fwd(q, k, v, dq, dk, dv, mask, scale=None, o=None, d_o=None, lse=No
         o=ptr(o), d_o=ptr(d_o) if tangent else None, lse=ptr(lse),
         q_stride_b=q.stride(0), q_stride_n=q.stride(1), q_stride_h=q.stride(2),
         k_stride_b=k.stride(0), k_stride_n=k.stride(1), k_stride_h=k.stride(2),
-        scale=float(scale) if scale is not None else 0.0)
+        scale=float(scale) if scale is not None else 0.0, d_lse=ptr(d_lse))
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    L = _lib.lib()
+    if max_splits == "auto":
+        n_cu = torch.cuda.get_device_properties(q.device).multi_processor_count
+        chosen = ctypes.c_int32(1)
+        _check(L.attn_jvp_split_choose(ctypes.byref(a), mask.handle, n_cu, ctypes.byref(chosen)),
+               "attn_jvp_split_choose")
+        max_splits = chosen.value
     with torch.cuda.device(q.device):
-        st = _lib.lib().attn_jvp_fwd(ctypes.byref(a), mask.handle, ctypes.c_void_p(handle))
-    _check(st, "attn_jvp_fwd")
+        if max_splits == 1 and workspace is None:
+            st = L.attn_jvp_fwd(ctypes.byref(a), mask.handle, ctypes.c_void_p(handle))
+            _check(st, "attn_jvp_fwd")
+        else:
+            need = ctypes.c_uint64(0)
+            _check(L.attn_jvp_fwd_split_workspace(ctypes.byref(a), mask.handle, int(max_splits),
+                                                  ctypes.byref(need)),
+                   "attn_jvp_fwd_split_workspace")
+            if workspace is None:
+                workspace = torch.empty(max(int(need.value), 16), dtype=torch.uint8,
+                                        device=q.device)
+            if not workspace.is_cuda or workspace.device != q.device:
+                raise ValueError("workspace must live on the device of q")
+            nbytes = workspace.numel() * workspace.element_size()
+            st = L.attn_jvp_fwd_split(ctypes.byref(a), mask.handle, int(max_splits),
+                                      ctypes.c_void_p(workspace.data_ptr()),
+                                      ctypes.c_uint64(nbytes), ctypes.c_void_p(handle))
+            _check(st, "attn_jvp_fwd_split")
+    if want_dlse:
+        return o, (d_o if tangent else None), lse, d_lse
     return o, (d_o if tangent else None), lse
+
+
+def _shape_args(q, k, tangent):
+    """Arguments carrying only the shapes and strides of q and k (for the
+    host-only queries: the pointers are placeholders, never dereferenced)."""
+    B, n_q, H, D = q.shape
+    fake = 1 << 20
+    return _lib.AttnJvpArgs(
+        dtype=_dtype_code(q), B=B, H=H, n_q=n_q, n_k=k.shape[1], D=D,
+        q=fake, k=2 * fake, v=3 * fake, dq=4 * fake if tangent else None,
+        o=5 * fake, d_o=6 * fake, lse=7 * fake,
+        q_stride_b=q.stride(0), q_stride_n=q.stride(1), q_stride_h=q.stride(2),
+        k_stride_b=k.stride(0), k_stride_n=k.stride(1), k_stride_h=k.stride(2), scale=0.0)
+
+
+def attn_jvp_split_choose(q, k, mask, n_cu, tangent=True):
+    """The max_splits attn_jvp_split_choose picks for tensors shaped like q
+    and k on a device with ``n_cu`` compute units (host-only)."""
+    chosen = ctypes.c_int32(0)
+    _check(_lib.lib().attn_jvp_split_choose(ctypes.byref(_shape_args(q, k, tangent)), mask.handle,
+                                            int(n_cu), ctypes.byref(chosen)),
+           "attn_jvp_split_choose")
+    return chosen.value
+
+
+def attn_jvp_fwd_split_workspace(q, k, mask, max_splits, tangent=True):
+    """Bytes of workspace attn_jvp_fwd with ``max_splits`` needs for tensors
+    shaped like q [B, n_q, H, D] and k [B, n_k, H, D] (host-only query: the
+    tensors may live on any device; nothing is launched)."""
+    a = _shape_args(q, k, tangent)
+    need = ctypes.c_uint64(0)
+    _check(_lib.lib().attn_jvp_fwd_split_workspace(ctypes.byref(a), mask.handle, int(max_splits),
+                                                   ctypes.byref(need)),
+           "attn_jvp_fwd_split_workspace")
+    return int(need.value)
+
+
+def attn_jvp_mask_split_schedule(mask, block_m, block_n, max_splits):
+    """Host copy of the unit list of a split-key launch (see the C header):
+    dict with unit_offsets, unit_order, unit_tile, unit_part (numpy int32)
+    and n_parts."""
+    import numpy as np
+    L = _lib.lib()
+    nu, npart = ctypes.c_int32(), ctypes.c_int32()
+    _check(L.attn_jvp_mask_split_schedule(mask.handle, block_m, block_n, max_splits,
+                                          ctypes.byref(nu), ctypes.byref(npart),
+                                          None, None, None, None),
+           "attn_jvp_mask_split_schedule")
+    arrs = {"unit_offsets": np.zeros(nu.value + 1, np.int32),
+            "unit_order": np.zeros(max(nu.value, 1), np.int32),
+            "unit_tile": np.zeros(max(nu.value, 1), np.int32),
+            "unit_part": np.zeros(max(nu.value, 1), np.int32)}
+    P = lambda x: x.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    _check(L.attn_jvp_mask_split_schedule(mask.handle, block_m, block_n, max_splits,
+                                          ctypes.byref(nu), ctypes.byref(npart),
+                                          P(arrs["unit_offsets"]), P(arrs["unit_order"]),
+                                          P(arrs["unit_tile"]), P(arrs["unit_part"])),
+           "attn_jvp_mask_split_schedule")
+    out = {k_: v_[:nu.value + 1] if k_ == "unit_offsets" else v_[:nu.value]
+           for k_, v_ in arrs.items()}
+    out["n_parts"] = npart.value
+    return out
 
 
 def attn_jvp_bwd(q, k, v, o, g_o, lse, mask, scale=None, g_q=None, g_k=None, g_v=None,

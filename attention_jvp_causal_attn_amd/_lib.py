@@ -38,6 +38,7 @@ class AttnJvpArgs(ctypes.Structure):
         ("q_stride_b", _i64), ("q_stride_n", _i64), ("q_stride_h", _i64),
         ("k_stride_b", _i64), ("k_stride_n", _i64), ("k_stride_h", _i64),
         ("scale", ctypes.c_float),
+        ("d_lse", _p),
     ]
 
 
@@ -63,9 +64,15 @@ SIGNATURES = {
     "attn_jvp_mask_export": (_i32, [_p, _pi32, _pi32, _pi32, _pi32]),
     "attn_jvp_mask_schedule": (_i32, [_p, _i32, _i32, _pi32, _pi64, _pi64, _pi32, _pi32,
                                       _pi32, _pi32, _pu32]),
+    "attn_jvp_mask_split_schedule": (_i32, [_p, _i32, _i32, _i32, _pi32, _pi32, _pi32, _pi32,
+                                            _pi32, _pi32]),
     "attn_jvp_mask_transpose": (_i32, [_p, _PPMASK]),
     "attn_jvp_mask_free": (None, [_p]),
     "attn_jvp_fwd": (_i32, [ctypes.POINTER(AttnJvpArgs), _p, _p]),
+    "attn_jvp_fwd_split_workspace": (_i32, [ctypes.POINTER(AttnJvpArgs), _p, _i32,
+                                            ctypes.POINTER(ctypes.c_uint64)]),
+    "attn_jvp_fwd_split": (_i32, [ctypes.POINTER(AttnJvpArgs), _p, _i32, _p, ctypes.c_uint64, _p]),
+    "attn_jvp_split_choose": (_i32, [ctypes.POINTER(AttnJvpArgs), _p, _i32, _pi32]),
     "attn_jvp_bwd": (_i32, [ctypes.POINTER(AttnJvpBwdArgs), _p, _p]),
     "attn_jvp_tile_shape": (_i32, [_i32, _i32, _pi32, _pi32]),
     "attn_jvp_status_str": (ctypes.c_char_p, [_i32]),

@@ -79,6 +79,61 @@ int device_schedule_locked(const attn_jvp_mask *m, int device, int BM, int BN,
   return ATTN_JVP_OK;
 }
 
+// Upload (once per device, tile shape and split count) the unit list of a
+// split-key launch; caller holds m->mu.
+int device_split_locked(const attn_jvp_mask *m, int device, int BM, int BN, int max_splits,
+                        const attnjvp::DeviceSplit **out) {
+  auto key = std::make_tuple(device, BM, BN, max_splits);
+  auto it = m->dev_split.find(key);
+  if (it != m->dev_split.end()) {
+    *out = &it->second;
+    return ATTN_JVP_OK;
+  }
+  int st = ATTN_JVP_OK;
+  const attnjvp::HostSplit *hp = attnjvp::host_split_locked(m, BM, BN, max_splits, &st);
+  if (!hp) return st;
+  const attnjvp::HostSplit &h = *hp;
+  const std::vector<int32_t> *parts[5] = {&h.unit_offsets, &h.unit_order, &h.unit_tile,
+                                          &h.unit_part, &h.split_tiles};
+  size_t at[5], total = 0;
+  for (int i = 0; i < 5; ++i) {
+    at[i] = total;
+    total += (parts[i]->size() * 4 + 15) & ~size_t(15);
+  }
+  total += 16;
+  std::vector<uint8_t> blob;
+  try {
+    blob.assign(total, 0);
+  } catch (const std::bad_alloc &) {
+    return ATTN_JVP_ERR_OOM;
+  }
+  for (int i = 0; i < 5; ++i)
+    if (!parts[i]->empty()) std::memcpy(blob.data() + at[i], parts[i]->data(), parts[i]->size() * 4);
+  void *dptr = nullptr;
+  hipError_t err = hipMalloc(&dptr, total);
+  if (err == hipErrorOutOfMemory) return ATTN_JVP_ERR_OOM;
+  if (err != hipSuccess) return ATTN_JVP_ERR_HIP;
+  err = hipMemcpy(dptr, blob.data(), total, hipMemcpyHostToDevice);
+  if (err != hipSuccess) {
+    (void)hipFree(dptr);
+    return ATTN_JVP_ERR_HIP;
+  }
+  attnjvp::DeviceSplit ds;
+  const uint8_t *b = static_cast<const uint8_t *>(dptr);
+  ds.base = dptr;
+  ds.unit_offsets = reinterpret_cast<const int32_t *>(b + at[0]);
+  ds.unit_order = reinterpret_cast<const int32_t *>(b + at[1]);
+  ds.unit_tile = reinterpret_cast<const int32_t *>(b + at[2]);
+  ds.unit_part = reinterpret_cast<const int32_t *>(b + at[3]);
+  ds.split_tiles = reinterpret_cast<const int32_t *>(b + at[4]);
+  ds.n_units = h.n_units;
+  ds.n_parts = h.n_parts;
+  ds.n_split = int32_t(h.split_tiles.size() / 4);
+  auto res = m->dev_split.emplace(key, ds);
+  *out = &res.first->second;
+  return ATTN_JVP_OK;
+}
+
 }  // namespace
 
 // Free the device schedules of a mask (and of its cached transpose).
@@ -89,8 +144,13 @@ static void free_device_schedules(attn_jvp_mask *m) {
     const int dev = std::get<0>(kv.first);
     if (hipSetDevice(dev) == hipSuccess) (void)hipFree(kv.second.base);
   }
-  if (have_cur && !m->dev_sched.empty()) (void)hipSetDevice(cur);
+  for (auto &kv : m->dev_split) {
+    const int dev = std::get<0>(kv.first);
+    if (hipSetDevice(dev) == hipSuccess) (void)hipFree(kv.second.base);
+  }
+  if (have_cur && !(m->dev_sched.empty() && m->dev_split.empty())) (void)hipSetDevice(cur);
   m->dev_sched.clear();
+  m->dev_split.clear();
   if (m->transposed) free_device_schedules(m->transposed.get());
 }
 
@@ -134,7 +194,8 @@ static void set_work_map(attnjvp::KernelParams &p) {
   p.map_slots = w.slots;
 }
 
-extern "C" int attn_jvp_fwd(const attn_jvp_args *a, const attn_jvp_mask *m, void *stream) {
+// Argument checks shared by the forward entry points (no device access).
+static int validate_fwd(const attn_jvp_args *a, const attn_jvp_mask *m, bool *tangent_out) {
   if (!a || !m) return ATTN_JVP_ERR_NULL;
   if (a->dtype != ATTN_JVP_BF16 && a->dtype != ATTN_JVP_F32) return ATTN_JVP_ERR_DTYPE;
   if (!a->q || !a->k || !a->v || !a->o || !a->lse) return ATTN_JVP_ERR_NULL;
@@ -158,34 +219,31 @@ extern "C" int attn_jvp_fwd(const attn_jvp_args *a, const attn_jvp_mask *m, void
   // rows of one head must not overlap the D contiguous elements of another
   if (a->H > 1 && (qs[2] < a->D || ks[2] < a->D)) return ATTN_JVP_ERR_SHAPE;
   const void *ins[6] = {a->q, a->k, a->v, a->dq, a->dk, a->dv};
-  const void *outs[2] = {a->o, a->d_o};
+  const void *outs[4] = {a->o, a->d_o, a->lse, a->d_lse};
   for (const void *p : ins)
     if (p && !aligned16(p)) return ATTN_JVP_ERR_ALIGN;
   for (const void *p : outs)
     if (p && !aligned16(p)) return ATTN_JVP_ERR_ALIGN;
-  if (!aligned16(a->lse)) return ATTN_JVP_ERR_ALIGN;
+  if (a->d_lse && !tangent) return ATTN_JVP_ERR_UNSUPPORTED;
   for (const void *p : ins)
     for (const void *o : outs)
       if (p && o && p == o) return ATTN_JVP_ERR_UNSUPPORTED;
-  if (tangent && a->o == a->d_o) return ATTN_JVP_ERR_UNSUPPORTED;
+  const int n_out = tangent ? 4 : 2;  // o, lse always; d_o and d_lse with a tangent
+  const void *live[4] = {a->o, a->lse, a->d_o, a->d_lse};
+  for (int i = 0; i < n_out; ++i)
+    for (int j = i + 1; j < n_out; ++j)
+      if (live[i] && live[i] == live[j]) return ATTN_JVP_ERR_UNSUPPORTED;
+  *tangent_out = tangent;
+  return ATTN_JVP_OK;
+}
 
-  int device = -1;
-  if (hipGetDevice(&device) != hipSuccess) return ATTN_JVP_ERR_HIP;
-  int BM = 0, BN = 0;
-  attn_jvp_tile_shape(a->dtype, a->D, &BM, &BN);
-  const DeviceSchedule *ds = nullptr;
-  {
-    std::lock_guard<std::mutex> lock(m->mu);
-    int st = device_schedule_locked(m, device, BM, BN, &ds);
-    if (st != ATTN_JVP_OK) return st;
-  }
-  if (int64_t(ds->n_tiles) * a->B * a->H > int64_t(0x7fffffff)) return ATTN_JVP_ERR_SHAPE;
-
+static KernelParams fwd_params(const attn_jvp_args *a, bool tangent, const DeviceSchedule *ds) {
   KernelParams p;
   p.q = a->q; p.k = a->k; p.v = a->v;
   p.dq = a->dq; p.dk = a->dk; p.dv = a->dv;
   p.o = a->o; p.d_o = tangent ? a->d_o : nullptr;
   p.lse = a->lse;
+  p.d_lse = tangent ? a->d_lse : nullptr;
   p.q_sb = a->q_stride_b; p.q_sn = a->q_stride_n; p.q_sh = a->q_stride_h;
   p.k_sb = a->k_stride_b; p.k_sn = a->k_stride_n; p.k_sh = a->k_stride_h;
   p.B = a->B; p.H = a->H; p.n_q = a->n_q; p.n_k = a->n_k;
@@ -198,9 +256,198 @@ extern "C" int attn_jvp_fwd(const attn_jvp_args *a, const attn_jvp_mask *m, void
   p.partial_bits = ds->partial_bits;
   p.n_tiles = ds->n_tiles;
   p.n_partial = ds->n_partial;
+  p.unit_tile = nullptr;
+  p.unit_part = nullptr;
+  p.part_stats = nullptr;
+  p.part_acc = nullptr;
+  p.n_parts = 0;
   set_work_map(p);
-  int err = a->dtype == ATTN_JVP_BF16 ? attnjvp::launch_bf16(p, a->D, tangent, stream)
-                                       : attnjvp::launch_f32(p, a->D, tangent, stream);
+  return p;
+}
+
+static int launch_fwd(const KernelParams &p, const attn_jvp_args *a, bool tangent, void *stream) {
+  const int err = a->dtype == ATTN_JVP_BF16 ? attnjvp::launch_bf16(p, a->D, tangent, stream)
+                                            : attnjvp::launch_f32(p, a->D, tangent, stream);
+  return err == hipSuccess ? ATTN_JVP_OK : ATTN_JVP_ERR_HIP;
+}
+
+extern "C" int attn_jvp_fwd(const attn_jvp_args *a, const attn_jvp_mask *m, void *stream) {
+  bool tangent = false;
+  int st = validate_fwd(a, m, &tangent);
+  if (st != ATTN_JVP_OK) return st;
+  int device = -1;
+  if (hipGetDevice(&device) != hipSuccess) return ATTN_JVP_ERR_HIP;
+  int BM = 0, BN = 0;
+  attn_jvp_tile_shape(a->dtype, a->D, &BM, &BN);
+  const DeviceSchedule *ds = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(m->mu);
+    st = device_schedule_locked(m, device, BM, BN, &ds);
+    if (st != ATTN_JVP_OK) return st;
+  }
+  if (int64_t(ds->n_tiles) * a->B * a->H > int64_t(0x7fffffff)) return ATTN_JVP_ERR_SHAPE;
+  return launch_fwd(fwd_params(a, tangent, ds), a, tangent, stream);
+}
+
+// Workspace bytes of a split launch with n_parts partial slots per slice:
+// float4 statistics, then 2 * D fp32 accumulators, per (slice, slot, row).
+static int64_t split_workspace_bytes(const attn_jvp_args *a, int BM, int64_t n_parts) {
+  const int64_t rows = int64_t(a->B) * a->H * n_parts * BM;
+  return rows * 16 + rows * 2 * a->D * 4;
+}
+
+extern "C" int attn_jvp_fwd_split_workspace(const attn_jvp_args *a, const attn_jvp_mask *m,
+                                            int32_t max_splits, uint64_t *bytes) {
+  if (!bytes) return ATTN_JVP_ERR_NULL;
+  bool tangent = false;
+  int st = validate_fwd(a, m, &tangent);
+  if (st != ATTN_JVP_OK) return st;
+  if (max_splits < 1) return ATTN_JVP_ERR_SHAPE;
+  int BM = 0, BN = 0;
+  attn_jvp_tile_shape(a->dtype, a->D, &BM, &BN);
+  std::lock_guard<std::mutex> lock(m->mu);
+  const attnjvp::HostSplit *h = attnjvp::host_split_locked(m, BM, BN, max_splits, &st);
+  if (!h) return st;
+  *bytes = uint64_t(split_workspace_bytes(a, BM, h->n_parts));
+  return ATTN_JVP_OK;
+}
+
+// Predicted time, in units of one key block, of running the unit list of a
+// split on `slots` concurrent workgroups: units start heaviest first, each on
+// the slot that frees up first (the dispatcher's behaviour for a grid larger
+// than the chip); a unit costs its entries plus a fixed start-up cost, and a
+// unit of a cut tile a further cost for its partial sums and their merge.
+static double predicted_blocks(const attnjvp::HostSplit &h, int64_t slices, int64_t slots) {
+  constexpr double kStart = 2.0, kPartial = 2.0;
+  std::vector<double> cost;
+  cost.reserve(h.unit_order.size());
+  for (int u : h.unit_order)
+    cost.push_back(double(h.unit_offsets[u + 1] - h.unit_offsets[u]) + kStart +
+                   (h.unit_part[u] >= 0 ? kPartial : 0.0));
+  // min-heap of slot finish times; every slice walks the same unit list
+  std::vector<double> heap(size_t(std::max<int64_t>(1, slots)), 0.0);
+  auto cmp = [](double x, double y) { return x > y; };
+  double makespan = 0.0;
+  for (int64_t s = 0; s < slices; ++s)
+    for (double c : cost) {
+      std::pop_heap(heap.begin(), heap.end(), cmp);
+      heap.back() += c;
+      makespan = std::max(makespan, heap.back());
+      std::push_heap(heap.begin(), heap.end(), cmp);
+    }
+  return makespan;
+}
+
+extern "C" int attn_jvp_split_choose(const attn_jvp_args *a, const attn_jvp_mask *m,
+                                     int32_t n_cu, int32_t *max_splits) {
+  if (!max_splits) return ATTN_JVP_ERR_NULL;
+  bool tangent = false;
+  int st = validate_fwd(a, m, &tangent);
+  if (st != ATTN_JVP_OK) return st;
+  if (n_cu < 1) return ATTN_JVP_ERR_SHAPE;
+  int BM = 0, BN = 0;
+  attn_jvp_tile_shape(a->dtype, a->D, &BM, &BN);
+  // workgroups resident per compute unit: one for the bf16 kernels (their
+  // registers fill the SIMDs), two for the fp32 kernel
+  const int64_t slots = int64_t(n_cu) * (a->dtype == ATTN_JVP_BF16 ? 1 : 2);
+  const int64_t slices = int64_t(a->B) * a->H;
+  std::lock_guard<std::mutex> lock(m->mu);
+  const attnjvp::HostSplit *h1 = attnjvp::host_split_locked(m, BM, BN, 1, &st);
+  if (!h1) return st;
+  // no split unless the grid leaves compute units idle: then splitting
+  // only adds partial sums
+  if (int64_t(h1->n_units) * slices >= 2 * slots) {
+    *max_splits = 1;
+    return ATTN_JVP_OK;
+  }
+  const double base = predicted_blocks(*h1, slices, slots);
+  int best = 1;
+  double best_t = base;
+  for (int S = 2; S <= 16; ++S) {
+    const attnjvp::HostSplit *h = attnjvp::host_split_locked(m, BM, BN, S, &st);
+    if (!h) return st;
+    const double t = predicted_blocks(*h, slices, slots);
+    if (t < best_t) {
+      best_t = t;
+      best = S;
+    }
+  }
+  // keep the plain launch unless the split is clearly faster
+  *max_splits = best_t < 0.85 * base ? best : 1;
+  return ATTN_JVP_OK;
+}
+
+extern "C" int attn_jvp_fwd_split(const attn_jvp_args *a, const attn_jvp_mask *m,
+                                  int32_t max_splits, void *workspace, uint64_t workspace_bytes,
+                                  void *stream) {
+  bool tangent = false;
+  int st = validate_fwd(a, m, &tangent);
+  if (st != ATTN_JVP_OK) return st;
+  if (max_splits < 1) return ATTN_JVP_ERR_SHAPE;
+  if (workspace && !aligned16(workspace)) return ATTN_JVP_ERR_ALIGN;
+  int BM = 0, BN = 0;
+  attn_jvp_tile_shape(a->dtype, a->D, &BM, &BN);
+  int64_t need = 0, n_units = 0, n_split = 0;
+  {
+    std::lock_guard<std::mutex> lock(m->mu);
+    const attnjvp::HostSplit *h = attnjvp::host_split_locked(m, BM, BN, max_splits, &st);
+    if (!h) return st;
+    need = split_workspace_bytes(a, BM, h->n_parts);
+    n_units = h->n_units;
+    n_split = int64_t(h->split_tiles.size() / 4);
+  }
+  if (need > 0 && !workspace) return ATTN_JVP_ERR_NULL;
+  if (uint64_t(need) > workspace_bytes) return ATTN_JVP_ERR_SHAPE;
+  const int64_t slices = int64_t(a->B) * a->H;
+  if (n_units * slices > int64_t(0x7fffffff) || n_split * slices * BM > int64_t(0x7fffffff))
+    return ATTN_JVP_ERR_SHAPE;
+  if (workspace) {
+    // the workspace must not overlap a tensor the launch reads or writes
+    const uintptr_t w0 = reinterpret_cast<uintptr_t>(workspace), w1 = w0 + uint64_t(need);
+    const void *ptrs[10] = {a->q, a->k, a->v, a->dq, a->dk, a->dv, a->o, a->d_o, a->lse, a->d_lse};
+    for (const void *q : ptrs) {
+      const uintptr_t x = reinterpret_cast<uintptr_t>(q);
+      if (q && x >= w0 && x < w1) return ATTN_JVP_ERR_UNSUPPORTED;
+    }
+  }
+  int device = -1;
+  if (hipGetDevice(&device) != hipSuccess) return ATTN_JVP_ERR_HIP;
+  const DeviceSchedule *ds = nullptr;
+  const attnjvp::DeviceSplit *sp = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(m->mu);
+    st = device_schedule_locked(m, device, BM, BN, &ds);
+    if (st != ATTN_JVP_OK) return st;
+    st = device_split_locked(m, device, BM, BN, max_splits, &sp);
+    if (st != ATTN_JVP_OK) return st;
+  }
+
+  KernelParams p = fwd_params(a, tangent, ds);
+  p.tile_offsets = sp->unit_offsets;
+  p.tile_order = sp->unit_order;
+  p.n_tiles = sp->n_units;
+  p.unit_tile = sp->unit_tile;
+  p.unit_part = sp->unit_part;
+  p.n_parts = sp->n_parts;
+  const int64_t rows = slices * sp->n_parts * BM;
+  p.part_stats = static_cast<float *>(workspace);
+  p.part_acc = sp->n_parts ? static_cast<float *>(workspace) + rows * 4 : nullptr;
+  set_work_map(p);
+  st = launch_fwd(p, a, tangent, stream);
+  if (st != ATTN_JVP_OK || sp->n_split == 0) return st;
+
+  attnjvp::MergeParams mp;
+  mp.o = a->o; mp.d_o = tangent ? a->d_o : nullptr;
+  mp.lse = a->lse; mp.d_lse = p.d_lse;
+  mp.q_sb = a->q_stride_b; mp.q_sn = a->q_stride_n; mp.q_sh = a->q_stride_h;
+  mp.B = a->B; mp.H = a->H; mp.n_q = a->n_q;
+  mp.block_m = BM;
+  mp.split_tiles = sp->split_tiles;
+  mp.n_split = sp->n_split;
+  mp.part_stats = p.part_stats;
+  mp.part_acc = p.part_acc;
+  mp.n_parts = sp->n_parts;
+  const int err = attnjvp::launch_merge(mp, a->D, a->dtype == ATTN_JVP_BF16, tangent, stream);
   return err == hipSuccess ? ATTN_JVP_OK : ATTN_JVP_ERR_HIP;
 }
 

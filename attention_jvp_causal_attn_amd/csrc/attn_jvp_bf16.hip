@@ -371,7 +371,8 @@ void attn_jvp_bf16_kernel(KernelParams p) {
   const int slot = L % p.n_tiles;
   const int bh = L / p.n_tiles;
   const int head = bh % p.H, batch = bh / p.H;
-  const int tile = p.tile_order[slot];
+  const int unit = p.tile_order[slot];  // a query tile, or a piece of one (split launch)
+  const int tile = p.unit_tile ? p.unit_tile[unit] : unit;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -389,7 +390,7 @@ void attn_jvp_bf16_kernel(KernelParams p) {
   const __bf16 *dkb_ = TAN && p.dk ? static_cast<const __bf16 *>(p.dk) + koff : nullptr;
   const __bf16 *dvb_ = TAN && p.dv ? static_cast<const __bf16 *>(p.dv) + koff : nullptr;
 
-  const int e0 = p.tile_offsets[tile], e1 = p.tile_offsets[tile + 1];
+  const int e0 = p.tile_offsets[unit], e1 = p.tile_offsets[unit + 1];
   const int n = e1 - e0;
   // Schedule entries of this tile, staged in LDS in chunks (read with LDS
   // loads inside the key loop, so no global load sits between the
@@ -480,11 +481,34 @@ void attn_jvp_bf16_kernel(KernelParams p) {
   const float l_tot = l_run + xor32(l_run);
   const float mu_tot = TAN ? mu_run + xor32(mu_run) : 0.f;
   if (!qvalid) return;
+  const int part = p.unit_part ? p.unit_part[unit] : -1;
+  if (part >= 0) {
+    // one piece of a split tile: running statistics and unnormalised sums,
+    // combined by the merge kernel
+    const int64_t prow = (int64_t(bh) * p.n_parts + part) * BM + row_in_tile;
+    if (hh == 0)
+      *reinterpret_cast<float4 *>(p.part_stats + prow * 4) = make_float4(m_ref, l_tot, mu_tot, 0.f);
+    float *pa = p.part_acc + prow * (2 * D);
+#pragma unroll
+    for (int nt = 0; nt < DT; ++nt) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d0 = 32 * nt + 8 * j + 4 * hh;
+        *reinterpret_cast<float4 *>(pa + d0) =
+            make_float4(accO[nt][4 * j], accO[nt][4 * j + 1], accO[nt][4 * j + 2], accO[nt][4 * j + 3]);
+        if (TAN)
+          *reinterpret_cast<float4 *>(pa + D + d0) =
+              make_float4(accT[nt][4 * j], accT[nt][4 * j + 1], accT[nt][4 * j + 2], accT[nt][4 * j + 3]);
+      }
+    }
+    return;
+  }
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const float mu_n = mu_tot * inv;
   if (hh == 0) {
-    p.lse[(int64_t(batch) * p.H + head) * p.n_q + qrow] =
-        l_tot > 0.f ? (m_ref + __log2f(l_tot)) * kLn2 : kNegInf;
+    const int64_t li = (int64_t(batch) * p.H + head) * p.n_q + qrow;
+    p.lse[li] = l_tot > 0.f ? (m_ref + __log2f(l_tot)) * kLn2 : kNegInf;
+    if (TAN && p.d_lse) p.d_lse[li] = mu_n;
   }
   const int64_t ooff = int64_t(batch) * p.q_sb + int64_t(head) * p.q_sh + int64_t(qrow) * p.q_sn;
   __bf16 *ob = static_cast<__bf16 *>(p.o) + ooff;

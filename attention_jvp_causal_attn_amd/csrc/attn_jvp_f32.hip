@@ -36,7 +36,8 @@ __global__ __launch_bounds__(kThreads) void attn_jvp_f32_kernel(KernelParams p) 
   const int slot = L % p.n_tiles;
   const int bh = L / p.n_tiles;
   const int head = bh % p.H, batch = bh / p.H;
-  const int tile = p.tile_order[slot];
+  const int unit = p.tile_order[slot];  // a query tile, or a piece of one (split launch)
+  const int tile = p.unit_tile ? p.unit_tile[unit] : unit;
 
   const int tid = threadIdx.x;
   const int row_in_tile = tid / TPR, part = tid % TPR;
@@ -62,7 +63,7 @@ __global__ __launch_bounds__(kThreads) void attn_jvp_f32_kernel(KernelParams p) 
   }
   float m_run = kNegInf, l_run = 0.f, mu_run = 0.f;
 
-  const int e0 = p.tile_offsets[tile], e1 = p.tile_offsets[tile + 1];
+  const int e0 = p.tile_offsets[unit], e1 = p.tile_offsets[unit + 1];
   for (int e = e0; e < e1; ++e) {
     const int2 ent = p.entries[e];
     const int key0 = ent.x * BN;
@@ -141,10 +142,29 @@ __global__ __launch_bounds__(kThreads) void attn_jvp_f32_kernel(KernelParams p) 
   }
 
   if (!qvalid) return;
+  const int slot_part = p.unit_part ? p.unit_part[unit] : -1;
+  if (slot_part >= 0) {
+    // one piece of a split tile: running statistics (natural units) and
+    // unnormalised sums, combined by the merge kernel
+    const int64_t prow = (int64_t(bh) * p.n_parts + slot_part) * BM + row_in_tile;
+    if (part == 0)
+      *reinterpret_cast<float4 *>(p.part_stats + prow * 4) =
+          make_float4(m_run, l_run, TAN ? mu_run : 0.f, 0.f);
+    float *pa = p.part_acc + prow * (2 * D) + d0;
+#pragma unroll
+    for (int x = 0; x < DS; ++x) {
+      pa[x] = acc[x];
+      if (TAN) pa[D + x] = tac[x];
+    }
+    return;
+  }
   const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
   const float mu_n = mu_run * inv;
-  if (part == 0)
-    p.lse[(int64_t(batch) * p.H + head) * p.n_q + qrow] = l_run > 0.f ? m_run + logf(l_run) : kNegInf;
+  if (part == 0) {
+    const int64_t li = (int64_t(batch) * p.H + head) * p.n_q + qrow;
+    p.lse[li] = l_run > 0.f ? m_run + logf(l_run) : kNegInf;
+    if (TAN && p.d_lse) p.d_lse[li] = mu_n;
+  }
   float *o = static_cast<float *>(p.o) + qoff + d0;
   float *dout = TAN ? static_cast<float *>(p.d_o) + qoff + d0 : nullptr;
 #pragma unroll

@@ -344,7 +344,88 @@ const HostSchedule *host_schedule_locked(const attn_jvp_mask *m, int block_m, in
   }
 }
 
+int split_schedule(const HostSchedule &s, int max_splits, HostSplit *out) {
+  if (max_splits < 1) return ATTN_JVP_ERR_SHAPE;
+  try {
+    HostSplit h;
+    int32_t longest = 0;
+    for (int t = 0; t < s.n_tiles; ++t)
+      longest = std::max(longest, s.tile_offsets[t + 1] - s.tile_offsets[t]);
+    h.unit_len = std::max<int32_t>(1, (longest + max_splits - 1) / max_splits);
+    h.unit_offsets.assign(1, 0);
+    for (int t = 0; t < s.n_tiles; ++t) {
+      const int32_t e0 = s.tile_offsets[t], n = s.tile_offsets[t + 1] - e0;
+      const int32_t k = std::max<int32_t>(1, (n + h.unit_len - 1) / h.unit_len);
+      // k near-equal consecutive runs (the first n % k one entry longer)
+      for (int32_t u = 0; u < k; ++u) {
+        h.unit_tile.push_back(t);
+        h.unit_part.push_back(k > 1 ? h.n_parts + u : -1);
+        h.unit_offsets.push_back(e0 + int32_t((int64_t(n) * (u + 1)) / k));
+      }
+      if (k > 1) {
+        h.split_tiles.insert(h.split_tiles.end(), {t, h.n_parts, k, 0});
+        h.n_parts += k;
+      }
+    }
+    h.n_units = int32_t(h.unit_tile.size());
+    h.unit_order.resize(h.n_units);
+    for (int u = 0; u < h.n_units; ++u) h.unit_order[u] = u;
+    std::stable_sort(h.unit_order.begin(), h.unit_order.end(), [&](int a, int b) {
+      return h.unit_offsets[a + 1] - h.unit_offsets[a] > h.unit_offsets[b + 1] - h.unit_offsets[b];
+    });
+    *out = std::move(h);
+  } catch (const std::bad_alloc &) {
+    return ATTN_JVP_ERR_OOM;
+  }
+  return ATTN_JVP_OK;
+}
+
+const HostSplit *host_split_locked(const attn_jvp_mask *m, int block_m, int block_n,
+                                   int max_splits, int *status) {
+  auto key = std::make_tuple(block_m, block_n, max_splits);
+  auto it = m->host_split.find(key);
+  if (it != m->host_split.end()) {
+    *status = ATTN_JVP_OK;
+    return &it->second;
+  }
+  const HostSchedule *s = host_schedule_locked(m, block_m, block_n, status);
+  if (!s) return nullptr;
+  HostSplit h;
+  *status = split_schedule(*s, max_splits, &h);
+  if (*status != ATTN_JVP_OK) return nullptr;
+  try {
+    auto res = m->host_split.emplace(key, std::move(h));
+    return &res.first->second;
+  } catch (const std::bad_alloc &) {
+    *status = ATTN_JVP_ERR_OOM;
+    return nullptr;
+  }
+}
+
 }  // namespace attnjvp
+
+extern "C" int attn_jvp_mask_split_schedule(const attn_jvp_mask *m, int32_t block_m,
+                                            int32_t block_n, int32_t max_splits,
+                                            int32_t *n_units, int32_t *n_parts,
+                                            int32_t *unit_offsets, int32_t *unit_order,
+                                            int32_t *unit_tile, int32_t *unit_part) {
+  if (!m || !n_units || !n_parts) return ATTN_JVP_ERR_NULL;
+  if (block_m <= 0 || block_n <= 0 || block_n % 32 || block_m > 4096 || block_n > 4096 ||
+      max_splits < 1)
+    return ATTN_JVP_ERR_SHAPE;
+  std::lock_guard<std::mutex> lock(m->mu);
+  int st = ATTN_JVP_OK;
+  const attnjvp::HostSplit *hp = attnjvp::host_split_locked(m, block_m, block_n, max_splits, &st);
+  if (!hp) return st;
+  const attnjvp::HostSplit &h = *hp;
+  *n_units = h.n_units;
+  *n_parts = h.n_parts;
+  if (unit_offsets) std::copy(h.unit_offsets.begin(), h.unit_offsets.end(), unit_offsets);
+  if (unit_order) std::copy(h.unit_order.begin(), h.unit_order.end(), unit_order);
+  if (unit_tile) std::copy(h.unit_tile.begin(), h.unit_tile.end(), unit_tile);
+  if (unit_part) std::copy(h.unit_part.begin(), h.unit_part.end(), unit_part);
+  return ATTN_JVP_OK;
+}
 
 extern "C" int attn_jvp_mask_schedule(const attn_jvp_mask *m, int32_t block_m, int32_t block_n,
                                       int32_t *n_tiles, int64_t *n_entries, int64_t *n_partial,

@@ -28,6 +28,34 @@ struct HostSchedule {
   int64_t n_partial = 0;
 };
 
+// The pieces (units) of a split-key launch, derived from a HostSchedule:
+// every query tile's entries are cut into consecutive runs of at most
+// unit_len entries (a tile without entries is one empty unit).
+struct HostSplit {
+  int32_t unit_len = 0;
+  int32_t n_units = 0;
+  int32_t n_parts = 0;                 // units of tiles that were cut
+  std::vector<int32_t> unit_offsets;   // n_units + 1, into the schedule's entries
+  std::vector<int32_t> unit_order;     // n_units, most entries first
+  std::vector<int32_t> unit_tile;      // n_units
+  std::vector<int32_t> unit_part;      // n_units, -1 for a tile's only unit
+  std::vector<int32_t> split_tiles;    // 4 per cut tile: tile, first slot, count, 0
+};
+
+// Device copy of a HostSplit (one allocation); entries and mask bits stay
+// those of the unsplit DeviceSchedule.
+struct DeviceSplit {
+  void *base = nullptr;
+  const int32_t *unit_offsets = nullptr;
+  const int32_t *unit_order = nullptr;
+  const int32_t *unit_tile = nullptr;
+  const int32_t *unit_part = nullptr;
+  const int32_t *split_tiles = nullptr;
+  int32_t n_units = 0;
+  int32_t n_parts = 0;
+  int32_t n_split = 0;
+};
+
 // One device copy of a schedule: a single allocation holding, in order,
 // tile_offsets, tile_order, entries (block, partial) interleaved, bits.
 struct DeviceSchedule {
@@ -65,6 +93,35 @@ struct KernelParams {
   int32_t map_group;
   int32_t map_slices;
   int32_t map_slots;
+  float *d_lse;  // optional tangent of LSE (JVP kernels only)
+  // Split-key launches: the schedule's "tiles" are pieces (units) of query
+  // tiles; unit_tile maps a unit to its query tile and unit_part to its
+  // partial slot (-1: the unit is its tile's only one and finishes itself).
+  // Units with a slot write float4 (m, l, mu, 0) per row to part_stats and
+  // the unnormalised accumulators (A, then T: 2 * D floats) per row to
+  // part_acc, at row (slice * n_parts + slot) * block_m + row in tile.  m is
+  // in the kernel's exponent base (bf16 kernels: log2 units of scale * q.k;
+  // fp32 kernel: natural units).  NULL unit_tile: units are the tiles.
+  const int32_t *unit_tile;
+  const int32_t *unit_part;
+  float *part_stats;
+  float *part_acc;
+  int32_t n_parts;
+};
+
+// The merge of split units: for every query tile that was cut, combine its
+// units' partials (rescaled to the largest m) and write O, dO, LSE, d_lse.
+struct MergeParams {
+  void *o, *d_o;
+  float *lse, *d_lse;
+  int64_t q_sb, q_sn, q_sh;
+  int32_t B, H, n_q;
+  int32_t block_m;
+  const int32_t *split_tiles;  // n_split x (tile, first slot, slot count, 0)
+  int32_t n_split;
+  const float *part_stats;
+  const float *part_acc;
+  int32_t n_parts;
 };
 
 // One grid's workgroup -> work item map (see work_item).
@@ -133,6 +190,10 @@ struct attn_jvp_mask {
   mutable std::map<std::pair<int, int>, attnjvp::HostSchedule> host_sched;
   // (device, block_m, block_n) -> device copy
   mutable std::map<std::tuple<int, int, int>, attnjvp::DeviceSchedule> dev_sched;
+  // (block_m, block_n, max_splits) -> host split schedule
+  mutable std::map<std::tuple<int, int, int>, attnjvp::HostSplit> host_split;
+  // (device, block_m, block_n, max_splits) -> device split schedule
+  mutable std::map<std::tuple<int, int, int, int>, attnjvp::DeviceSplit> dev_split;
   // the transposed mask (keys as rows), built on first use by the backward
   mutable std::unique_ptr<attn_jvp_mask> transposed;
 };
@@ -147,12 +208,22 @@ int transpose_mask(const attn_jvp_mask *m, attn_jvp_mask **out);
 const HostSchedule *host_schedule_locked(const attn_jvp_mask *m, int block_m,
                                          int block_n, int *status);
 
+// Cut the tiles of a schedule into units of at most
+// ceil(max entries of a tile / max_splits) entries (max_splits >= 1).
+int split_schedule(const HostSchedule &s, int max_splits, HostSplit *out);
+
+// Build (or fetch the cached) split of the (block_m, block_n) schedule;
+// caller holds m->mu.
+const HostSplit *host_split_locked(const attn_jvp_mask *m, int block_m, int block_n,
+                                   int max_splits, int *status);
+
 // Kernel launchers (defined in the .hip files).  Return a hipError_t value.
 int launch_bf16(const KernelParams &p, int D, bool tangent, void *stream);
 int launch_bf16_wide(const KernelParams &p, bool tangent, void *stream);  // D = 128
 int launch_bwd_bf16(const BwdParams &p, int D, void *stream);
 int launch_bwd_bf16_wide(const BwdParams &p, void *stream);  // D = 128
 int launch_f32(const KernelParams &p, int D, bool tangent, void *stream);
+int launch_merge(const MergeParams &p, int D, bool bf16, bool tangent, void *stream);
 
 // Tile shapes of the kernels.
 constexpr int kBf16BlockM = 128;      // head dim 64: 4 waves x 32 rows

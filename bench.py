@@ -116,6 +116,41 @@ def cpu_baseline(w, x, target_s=18.0):
                        f"({pairs} admissible pairs, {dt:.1f} s), scaled by 12*D FLOP per pair")}
 
 
+def bench_split(w, args, stream):
+    """The split-key launch where it matters: frame-wise generation with a KV
+    cache, the last frame's queries (one frame of tokens) against the cached
+    20 clean frames plus itself, every key admissible.  Few query tiles meet
+    long key lists, so the unsplit grid leaves compute units idle."""
+    import torch
+    import attention_jvp_causal_attn_amd as aj
+    from attention_jvp_causal_attn_amd.inputs import make_random
+    n_q, n_k = w.tokens_per_frame, 21 * w.tokens_per_frame
+    xq = make_random(1, n_q, w.H, w.D, dtype=w.dtype, seed=31, tangent_std=0.1, device="cuda")
+    xk = make_random(1, n_k, w.H, w.D, dtype=w.dtype, seed=41, tangent_std=0.1, device="cuda")
+    m = aj.attn_jvp_mask_rects(n_q, n_k, [0, n_q], [0, 1], [0], [n_k])
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    S = aj.attn_jvp_split_choose(xq["q"], xk["k"], m, n_cu)
+    ws = torch.empty(max(16, aj.attn_jvp_fwd_split_workspace(xq["q"], xk["k"], m, S)),
+                     dtype=torch.uint8, device="cuda")
+    o, do = torch.empty_like(xq["q"]), torch.empty_like(xq["q"])
+    lse = torch.empty(1, w.H, n_q, dtype=torch.float32, device="cuda")
+
+    def run(splits):
+        return lambda: aj.attn_jvp_fwd(xq["q"], xk["k"], xk["v"], xq["dq"], xk["dk"], xk["dv"],
+                                       m, o=o, d_o=do, lse=lse, stream=stream,
+                                       max_splits=splits, workspace=ws if splits > 1 else None)
+
+    flops = 12 * w.D * n_q * n_k * w.H
+    ums, _ = time_calls(run(1), args.steps, args.warmup, stream)
+    sms, _ = time_calls(run(S), args.steps, args.warmup, stream)
+    log(f"KV-cache last frame ({n_q} x {n_k}): unsplit {ums:.3f} ms, "
+        f"max_splits={S} {sms:.3f} ms ({flops / sms / 1e9:.1f} TFLOP/s)")
+    return {"n_q": n_q, "n_k": n_k, "H": w.H, "D": w.D, "max_splits": S,
+            "unsplit_ms": round(ums, 4), "split_ms": round(sms, 4),
+            "unsplit_tflops": round(flops / ums / 1e9, 2),
+            "split_tflops": round(flops / sms / 1e9, 2)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -125,6 +160,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-primal", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-split", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter scaling)")
     args = ap.parse_args()
@@ -222,6 +258,8 @@ def main():
         log(f"backward: {bms:.3f} ms/call, {bval:.1f} TFLOP/s (10*D FLOP per pair)")
         res["backward"] = {"ms_per_step": round(bms, 4), "tflops": round(bval, 2),
                            "flop_per_pair": 10 * w.D}
+    if not args.no_split:
+        res["kv_cache_last_frame"] = bench_split(w, args, stream)
     traffic = measured_traffic(w.name)
     res["roofline"] = {"bound": "mfma", "achieved": round(value, 2), "peak": PEAK_BF16_TFLOPS,
                        "unit": "TFLOP/s", "frac": round(value / PEAK_BF16_TFLOPS, 4),

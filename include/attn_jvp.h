@@ -140,6 +140,24 @@ int attn_jvp_mask_schedule(const attn_jvp_mask *m, int32_t block_m,
                            int32_t *entry_block, int32_t *entry_partial,
                            uint32_t *partial_bits);
 
+/* Host copy of the unit list attn_jvp_fwd_split launches for max_splits
+ * (for tests and tools).  With L = max(1, ceil(longest / max_splits)),
+ * longest the largest entry count of any tile of the (block_m, block_n)
+ * schedule, tile t with n entries becomes k = max(1, ceil(n / L)) units,
+ * entries tile_offsets[t] + floor(n*u/k) .. tile_offsets[t] + floor(n*(u+1)/k)
+ * - 1 for u = 0 .. k-1, listed tile by tile: unit_offsets[n_units + 1] holds
+ * these boundaries, unit_tile[n_units] the tile, unit_part[n_units] the
+ * partial slot (consecutive from 0 over the units of tiles with k > 1; -1 for
+ * a tile's only unit), unit_order[n_units] the units by decreasing entry
+ * count (ties by index).  *n_parts counts the slots.  Call with NULL arrays
+ * for the sizes first.  Errors: ERR_NULL, ERR_SHAPE (as for
+ * attn_jvp_mask_schedule, or max_splits < 1), ERR_OOM. */
+int attn_jvp_mask_split_schedule(const attn_jvp_mask *m, int32_t block_m,
+                                 int32_t block_n, int32_t max_splits,
+                                 int32_t *n_units, int32_t *n_parts,
+                                 int32_t *unit_offsets, int32_t *unit_order,
+                                 int32_t *unit_tile, int32_t *unit_part);
+
 /* The transposed mask: key and query roles swapped (its n_q is m's n_k):
  * key j admits query i exactly when query i admits key j under m.  The
  * backward pass walks it (key tiles over query blocks).  On success *out owns
@@ -172,6 +190,10 @@ typedef struct attn_jvp_args {
   int64_t q_stride_b, q_stride_n, q_stride_h;
   int64_t k_stride_b, k_stride_n, k_stride_h;
   float scale;              /* softmax scale; <= 0 selects 1/sqrt(D) */
+  float *d_lse;             /* optional output: the tangent of LSE, [B, H, n_q]
+                               fp32 contiguous, sum_j p_ij ds_ij (0 for rows
+                               without keys); NULL = not written.  Needs at
+                               least one tangent (ERR_UNSUPPORTED otherwise). */
 } attn_jvp_args;
 
 /* Launch the fused primal + tangent pass on hip_stream (a hipStream_t; NULL
@@ -185,6 +207,44 @@ typedef struct attn_jvp_args {
  * differ from n_q/n_k), ERR_UNSUPPORTED, ERR_HIP, ERR_OOM. */
 int attn_jvp_fwd(const attn_jvp_args *a, const attn_jvp_mask *m,
                  void *hip_stream);
+
+/* Split-key variant of attn_jvp_fwd, same arguments and results ("Causal-rCM
+ * ..." Appendix B: the kernel works through a tile's admissible key ranges in
+ * parallel).  Each query tile's list of key blocks (attn_jvp_mask_schedule) is
+ * cut into consecutive pieces of at most ceil(max_blocks / max_splits) blocks,
+ * max_blocks being the longest list of any tile, and every piece runs as a
+ * workgroup of its own, so long rows no longer serialise on one compute unit
+ * (few query tiles against many keys, e.g. one chunk of queries against a
+ * cached prefix).  The pieces of a tile that was cut write their running max,
+ * sums l and mu and unnormalised accumulators to the workspace; a second
+ * kernel merges them (rescaled to their common max) into O, dO, LSE and d_lse.
+ * Tiles left whole finish as in attn_jvp_fwd.  max_splits = 1 gives exactly
+ * attn_jvp_fwd's results; otherwise results agree with it up to fp32
+ * rounding of the reordered sums.  Deterministic.
+ *
+ * workspace: caller-owned device memory, 16-byte aligned, of at least the
+ * size attn_jvp_fwd_split_workspace reports for the same arguments, mask and
+ * max_splits (0 bytes, and NULL allowed, when no tile is cut).  It holds
+ * scratch only: nothing needs clearing, and calls sharing one workspace must
+ * be ordered on one stream.  Errors: those of attn_jvp_fwd, ERR_SHAPE
+ * (max_splits < 1, or workspace_bytes below the required size), ERR_NULL
+ * (workspace NULL while bytes are needed), ERR_ALIGN (workspace). */
+int attn_jvp_fwd_split_workspace(const attn_jvp_args *a, const attn_jvp_mask *m,
+                                 int32_t max_splits, uint64_t *bytes);
+int attn_jvp_fwd_split(const attn_jvp_args *a, const attn_jvp_mask *m,
+                       int32_t max_splits, void *workspace,
+                       uint64_t workspace_bytes, void *hip_stream);
+
+/* A max_splits for attn_jvp_fwd_split on a device with n_cu compute units
+ * (host-only: nothing is launched).  Returns 1 when the unsplit grid has at
+ * least two workgroups per resident slot; otherwise, among 1 .. 16, the count
+ * whose unit list has the smallest predicted makespan (units heaviest first
+ * on the slot that frees up first, cost = key blocks + a fixed start-up cost,
+ * plus a partial-sum cost for units of cut tiles), if it beats the unsplit
+ * prediction by more than 15 %, else 1.  Errors: those of attn_jvp_fwd's
+ * argument checks, ERR_NULL (max_splits), ERR_SHAPE (n_cu < 1), ERR_OOM. */
+int attn_jvp_split_choose(const attn_jvp_args *a, const attn_jvp_mask *m,
+                          int32_t n_cu, int32_t *max_splits);
 
 /* Arguments of one backward call: the gradients of L = sum(g_o * O) with
  * respect to Q, K and V for the masked attention O = attn(Q, K, V) of the

@@ -94,6 +94,11 @@ BAD = [
     (dict(d_o=0x70000), _lib.ATTN_JVP_ERR_UNSUPPORTED),    # d_o aliases o
     (dict(scale=float("nan")), _lib.ATTN_JVP_ERR_SHAPE),
     (dict(scale=float("inf")), _lib.ATTN_JVP_ERR_SHAPE),
+    (dict(d_lse=0xa0004), _lib.ATTN_JVP_ERR_ALIGN),
+    (dict(d_lse=0xa0000, dq=None, dk=None, dv=None), _lib.ATTN_JVP_ERR_UNSUPPORTED),  # no tangent
+    (dict(d_lse=0x90000), _lib.ATTN_JVP_ERR_UNSUPPORTED),   # d_lse aliases lse
+    (dict(lse=0x70000), _lib.ATTN_JVP_ERR_UNSUPPORTED),     # lse aliases o
+    (dict(d_lse=0x30000), _lib.ATTN_JVP_ERR_UNSUPPORTED),   # d_lse aliases v
 ]
 
 
@@ -101,6 +106,53 @@ BAD = [
 def test_fwd_rejects_bad_arguments(kw, status):
     mask = aj.attn_jvp_mask_tf(4, 16, 1)
     assert _fwd(_args(mask, **kw), mask) == status
+
+
+def _split(a, mask, S, ws=None, nbytes=0):
+    return _lib.lib().attn_jvp_fwd_split(ctypes.byref(a), mask.handle, S, ws, nbytes, None)
+
+
+@pytest.mark.parametrize("kw,status", BAD)
+def test_split_rejects_bad_arguments(kw, status):
+    mask = aj.attn_jvp_mask_tf(4, 16, 1)
+    assert _split(_args(mask, **kw), mask, 2, 0x100000, 1 << 30) == status
+
+
+def test_split_workspace_checks():
+    mask = aj.attn_jvp_mask_tf(8, 64, 1)   # n = 1024: 8 tiles of 128 rows at D=64
+    L = _lib.lib()
+    a = _args(mask, D=64, q_stride_n=128, q_stride_h=64, k_stride_n=128, k_stride_h=64)
+    need = ctypes.c_uint64(0)
+    assert L.attn_jvp_fwd_split_workspace(ctypes.byref(a), mask.handle, 4,
+                                          ctypes.byref(need)) == _lib.ATTN_JVP_OK
+    u = aj.attn_jvp_mask_split_schedule(mask, 128, 32, 4)
+    assert u["n_parts"] > 0
+    rows = 1 * 2 * u["n_parts"] * 128                      # B * H * parts * block_m
+    assert need.value == rows * 16 + rows * 2 * 64 * 4      # float4 stats + A, T rows
+    assert L.attn_jvp_fwd_split_workspace(ctypes.byref(a), mask.handle, 0,
+                                          ctypes.byref(need)) == _lib.ATTN_JVP_ERR_SHAPE
+    assert L.attn_jvp_fwd_split_workspace(ctypes.byref(a), mask.handle, 4,
+                                          None) == _lib.ATTN_JVP_ERR_NULL
+    assert L.attn_jvp_fwd_split_workspace(ctypes.byref(a), mask.handle, 1,
+                                          ctypes.byref(need)) == _lib.ATTN_JVP_OK
+    assert need.value == 0
+    big = 1 << 40
+    assert L.attn_jvp_fwd_split_workspace(ctypes.byref(a), mask.handle, 4,
+                                          ctypes.byref(need)) == _lib.ATTN_JVP_OK
+    assert _split(a, mask, 0, big, need.value) == _lib.ATTN_JVP_ERR_SHAPE
+    assert _split(a, mask, 4, None, need.value) == _lib.ATTN_JVP_ERR_NULL
+    assert _split(a, mask, 4, big + 8, need.value) == _lib.ATTN_JVP_ERR_ALIGN
+    assert _split(a, mask, 4, big, need.value - 16) == _lib.ATTN_JVP_ERR_SHAPE
+    # the workspace may not contain a tensor
+    assert _split(a, mask, 4, 0x8000, need.value) == _lib.ATTN_JVP_ERR_UNSUPPORTED
+
+
+@pytest.mark.skipif(_gpu_present(), reason="needs a host without a HIP device")
+def test_split_without_device_reports_hip_error():
+    mask = aj.attn_jvp_mask_tf(4, 16, 1)
+    a = _args(mask)
+    assert _split(a, mask, 1) == _lib.ATTN_JVP_ERR_HIP
+    assert _split(a, mask, 2, 1 << 40, 1 << 30) == _lib.ATTN_JVP_ERR_HIP
 
 
 def test_fwd_null_args_and_mask():
@@ -172,3 +224,28 @@ def test_bwd_without_device_reports_hip_error():
     mask = aj.attn_jvp_mask_tf(4, 16, 1)
     a = _bwd_args(mask)
     assert _lib.lib().attn_jvp_bwd(ctypes.byref(a), mask.handle, None) == _lib.ATTN_JVP_ERR_HIP
+
+
+def test_split_choose():
+    import torch
+    bf = lambda n, D=128: torch.empty(1, n, 12, D, dtype=torch.bfloat16)
+    # one frame of queries (7 tiles of 256 rows) against 32,760 keys (1,024
+    # blocks of 32), 12 heads, 256 compute units: 84 workgroups leave the chip
+    # idle.  By hand: S = 3 gives 252 units of <= 342 blocks, one round
+    # (342 + 2 + 2); S = 2: 168 units of 512; S = 4: 336 units, two rounds of
+    # 256; S = 6: 504 units, two rounds of 171; S = 9: 756 units, three
+    # rounds of 114; S = 12: 1008 units, four rounds of 86.
+    m = aj.attn_jvp_mask_rects(1560, 32760, [0, 1560], [0, 1], [0], [32760])
+    assert aj.attn_jvp_split_choose(bf(1560), bf(32760), m, 256) == 3
+    # a grid of many tiles per compute unit is never split
+    tf = aj.attn_jvp_mask_tf(21, 1560, 3)
+    assert aj.attn_jvp_split_choose(bf(65520), bf(65520), tf, 256) == 1
+    assert aj.attn_jvp_split_choose(bf(1560), bf(32760), m, 8) == 1
+    L = _lib.lib()
+    a = _args(m, n_q=1560, n_k=32760)
+    out = ctypes.c_int32()
+    assert L.attn_jvp_split_choose(ctypes.byref(a), m.handle, 0, ctypes.byref(out)) == \
+        _lib.ATTN_JVP_ERR_SHAPE
+    assert L.attn_jvp_split_choose(ctypes.byref(a), m.handle, 256, None) == _lib.ATTN_JVP_ERR_NULL
+    assert L.attn_jvp_split_choose(ctypes.byref(_args(m, n_q=1560, n_k=32760, D=96)), m.handle,
+                                   256, ctypes.byref(out)) == _lib.ATTN_JVP_ERR_UNSUPPORTED

@@ -1,0 +1,233 @@
+"""GPU parity of the split-key launch (attn_jvp_fwd_split) and of the LSE
+tangent output against the fp64 oracle.
+
+Tolerances as for the unsplit launch: per output tensor (O, dO, LSE, dLSE)
+max|gpu - ref| <= tol * max|ref|, tol = 2e-2 for bf16 inputs and 1e-5 for
+fp32 inputs.  max_splits = 1 must reproduce attn_jvp_fwd bit for bit.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import attention_jvp_causal_attn_amd as aj
+from attention_jvp_causal_attn_amd.inputs import WORKLOADS, make_inputs, make_random
+from oracle import (block_causal_allowed, masked_attention, masked_attention_jvp,
+                    rects_allowed, tf_allowed)
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 2e-2, "f32": 1e-5}
+DEV = "cuda"
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def f64(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def check(name, got, ref, tol):
+    got = np.asarray(got, dtype=np.float64)
+    fin = np.isfinite(ref)
+    assert np.array_equal(np.isfinite(got), fin), f"{name}: finite pattern differs"
+    if not fin.any():
+        return 0.0
+    err = np.abs(got[fin] - ref[fin]).max()
+    scale = np.abs(ref[fin]).max()
+    rel = err / scale if scale > 0 else err
+    say(f"  {name}: max|err| = {err:.3e}, max|ref| = {scale:.3e}, ratio = {rel:.3e} (tol {tol})")
+    assert rel <= tol, f"{name}: {rel:.3e} > {tol}"
+    return rel
+
+
+def fwd(xd, mask, S, tangents=("dq", "dk", "dv"), lse_tangent=True):
+    t = {n: (xd[n] if n in tangents else None) for n in ("dq", "dk", "dv")}
+    out = aj.attn_jvp_fwd(xd["q"], xd["k"], xd["v"], t["dq"], t["dk"], t["dv"], mask,
+                          max_splits=S, lse_tangent=lse_tangent and bool(tangents))
+    torch.cuda.synchronize()
+    return out
+
+
+def parity(x, pred, mask, S, dtype, rows=None):
+    xd = {k: v.to(DEV) for k, v in x.items()}
+    o, do, lse, dlse = fwd(xd, mask, S)
+    O, dO, LSE, dL = masked_attention_jvp(x["q"], x["k"], x["v"], x["dq"], x["dk"], x["dv"],
+                                          pred, rows=rows, lse_tangent=True)
+    sel = slice(None) if rows is None else torch.as_tensor(rows)
+    tol = TOL[dtype]
+    check("O", f64(o[:, sel]), O, tol)
+    check("dO", f64(do[:, sel]), dO, tol)
+    check("LSE", f64(lse[:, :, sel]), LSE, tol)
+    check("dLSE", f64(dlse[:, :, sel]), dL, tol)
+    return o, do, lse, dlse
+
+
+CASES = [  # dtype, D, TF (nf, tpf, fpc), B, H
+    ("bf16", 128, (5, 137, 1), 1, 2),   # N = 1370: 6 tiles of 256 rows, ragged tail
+    ("bf16", 64, (6, 93, 2), 2, 1),     # 128-row tiles
+    ("f32", 64, (4, 70, 2), 1, 2),      # 64-row tiles, natural-log partials
+    ("f32", 128, (3, 50, 1), 1, 1),
+]
+
+
+@pytest.mark.parametrize("S", [2, 3, 8])
+@pytest.mark.parametrize("dtype,D,tf,B,H", CASES)
+def test_split_tf_matches_oracle(dtype, D, tf, B, H, S):
+    say(f"case: split S={S} {dtype} D={D} TF {tf} B={B} H={H}")
+    pred = tf_allowed(*tf)
+    x = make_random(B, pred.n_q, H, D, dtype=dtype, seed=12000 + 7 * S + D, tangent_std=0.1)
+    parity(x, pred, aj.attn_jvp_mask_tf(*tf), S, dtype)
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("bf16", 64), ("f32", 64)])
+def test_one_split_is_the_unsplit_launch(dtype, D):
+    say(f"case: max_splits=1 vs attn_jvp_fwd, {dtype} D={D}")
+    pred = tf_allowed(5, 61, 1)
+    mask = aj.attn_jvp_mask_tf(5, 61, 1)
+    x = make_random(1, pred.n_q, 2, D, dtype=dtype, seed=12100 + D, tangent_std=0.1)
+    xd = {k: v.to(DEV) for k, v in x.items()}
+    ws = torch.empty(16, dtype=torch.uint8, device=DEV)   # nothing is cut: no bytes needed
+    assert aj.attn_jvp_fwd_split_workspace(xd["q"], xd["k"], mask, 1) == 0
+    a = aj.attn_jvp_fwd(xd["q"], xd["k"], xd["v"], xd["dq"], xd["dk"], xd["dv"], mask,
+                        max_splits=1, workspace=ws, lse_tangent=True)
+    b = aj.attn_jvp_fwd(xd["q"], xd["k"], xd["v"], xd["dq"], xd["dk"], xd["dv"], mask,
+                        lse_tangent=True)
+    torch.cuda.synchronize()
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("bf16", 64), ("f32", 128)])
+def test_kv_cache_chunk_split(dtype, D):
+    # one chunk of queries against a cached prefix plus itself: few query
+    # tiles, long key lists, every tile cut
+    n_q, n_k, H = 300, 1500, 2
+    say(f"case: KV-cache rectangle n_q={n_q} n_k={n_k} {dtype} D={D}, S=4")
+    xq = make_random(1, n_q, H, D, dtype=dtype, seed=12200 + D, tangent_std=0.1)
+    xk = make_random(1, n_k, H, D, dtype=dtype, seed=12300 + D, tangent_std=0.1)
+    x = dict(q=xq["q"], dq=xq["dq"], k=xk["k"], v=xk["v"], dk=xk["dk"], dv=xk["dv"])
+    # detached cache: zero key/value tangents on the cached prefix
+    x["dk"][:, :n_k - n_q] = 0
+    x["dv"][:, :n_k - n_q] = 0
+    mask = aj.attn_jvp_mask_rects(n_q, n_k, [0, n_q], [0, 1], [0], [n_k])
+    parity(x, rects_allowed(n_q, n_k, [(0, n_q, 0, n_k)]), mask, 4, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_split_rows_without_keys(dtype):
+    # rows 256..299 see nothing: their tile is one empty unit, O = dO = 0,
+    # LSE = -inf, dLSE = 0
+    gq, rp, kb, ke = [0, 256, 300], [0, 1, 1], [0], [900]
+    pred = rects_allowed(300, 900, [(0, 256, 0, 900)])
+    x = make_random(1, 300, 1, 128, dtype=dtype, seed=12400, tangent_std=0.1)
+    xk = make_random(1, 900, 1, 128, dtype=dtype, seed=12401, tangent_std=0.1)
+    for n in ("k", "v", "dk", "dv"):
+        x[n] = xk[n]
+    o, do, lse, dlse = parity(x, pred, aj.attn_jvp_mask_rects(300, 900, gq, rp, kb, ke), 4, dtype)
+    assert torch.all(o[:, 256:] == 0) and torch.all(do[:, 256:] == 0)
+    assert torch.all(torch.isneginf(lse[:, :, 256:])) and torch.all(dlse[:, :, 256:] == 0)
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 64)])
+def test_split_primal_only_and_partial_tangents(dtype, D):
+    pred = block_causal_allowed(7, 90)
+    mask = aj.attn_jvp_mask_block_causal(7, 90)
+    x = make_random(1, pred.n_q, 2, D, dtype=dtype, seed=12500 + D, tangent_std=0.1)
+    xd = {k: v.to(DEV) for k, v in x.items()}
+    say(f"case: split primal only, {dtype} D={D}")
+    o, do, lse = fwd(xd, mask, 3, tangents=())
+    assert do is None
+    O, LSE = masked_attention(x["q"], x["k"], x["v"], pred)
+    check("O", f64(o), O, TOL[dtype])
+    check("LSE", f64(lse), LSE, TOL[dtype])
+    say(f"case: split with dq only, {dtype} D={D}")
+    o, do, lse, dlse = fwd(xd, mask, 3, tangents=("dq",))
+    z = torch.zeros_like(x["dk"])
+    O, dO, LSE, dL = masked_attention_jvp(x["q"], x["k"], x["v"], x["dq"], z, z, pred,
+                                          lse_tangent=True)
+    check("O", f64(o), O, TOL[dtype])
+    check("dO", f64(do), dO, TOL[dtype])
+    check("dLSE", f64(dlse), dL, TOL[dtype])
+
+
+def test_split_deterministic_and_workspace_reuse():
+    pred = tf_allowed(6, 70, 2)
+    mask = aj.attn_jvp_mask_tf(6, 70, 2)
+    x = make_random(1, pred.n_q, 2, 128, dtype="bf16", seed=12600, tangent_std=0.1)
+    xd = {k: v.to(DEV) for k, v in x.items()}
+    need = aj.attn_jvp_fwd_split_workspace(xd["q"], xd["k"], mask, 4)
+    assert need > 0
+    ws = torch.full((need,), 255, dtype=torch.uint8, device=DEV)   # stale contents
+    a = aj.attn_jvp_fwd(xd["q"], xd["k"], xd["v"], xd["dq"], xd["dk"], xd["dv"], mask,
+                        max_splits=4, workspace=ws, lse_tangent=True)
+    b = aj.attn_jvp_fwd(xd["q"], xd["k"], xd["v"], xd["dq"], xd["dk"], xd["dv"], mask,
+                        max_splits=4, workspace=ws, lse_tangent=True)
+    torch.cuda.synchronize()
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
+    with pytest.raises(aj.AttnJvpError):
+        aj.attn_jvp_fwd(xd["q"], xd["k"], xd["v"], xd["dq"], xd["dk"], xd["dv"], mask,
+                        max_splits=4, workspace=ws[:need - 16])
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("bf16", 64), ("f32", 64)])
+def test_lse_tangent_unsplit(dtype, D):
+    say(f"case: dLSE from attn_jvp_fwd, {dtype} D={D}")
+    pred = tf_allowed(5, 37, 1)
+    x = make_random(1, pred.n_q, 2, D, dtype=dtype, seed=12700 + D, tangent_std=0.1)
+    xd = {k: v.to(DEV) for k, v in x.items()}
+    o, do, lse, dlse = aj.attn_jvp_fwd(xd["q"], xd["k"], xd["v"], xd["dq"], xd["dk"], xd["dv"],
+                                       aj.attn_jvp_mask_tf(5, 37, 1), lse_tangent=True)
+    torch.cuda.synchronize()
+    *_, dL = masked_attention_jvp(x["q"], x["k"], x["v"], x["dq"], x["dk"], x["dv"], pred,
+                                  lse_tangent=True)
+    check("dLSE", f64(dlse), dL, TOL[dtype])
+
+
+def test_full_size_chunkwise_split_sampled():
+    # the 65,520-token chunk-wise workload with its heavy tiles cut in two
+    w = WORKLOADS[3]
+    say(f"case: split S=2 on workload 3: {w.describe()}")
+    x = make_inputs(w)
+    mask = aj.attn_jvp_mask_tf(w.n_frames, w.tokens_per_frame, w.frames_per_chunk)
+    pred = tf_allowed(w.n_frames, w.tokens_per_frame, w.frames_per_chunk)
+    rng = np.random.default_rng(3)
+    Nc, C = w.n_frames * w.tokens_per_frame, w.unit_tokens
+    rows = {0, w.N - 1, Nc - 1, Nc, Nc + C, 2 * C - 1}
+    rows.update(rng.integers(0, w.N, size=40).tolist())
+    rows = np.array(sorted(rows))
+    parity(x, pred, mask, 2, "bf16", rows=rows)
+
+
+def test_full_size_kv_cache_chunk_sampled():
+    # one 3-frame chunk (4,680 queries) against the 65,520-token sequence,
+    # H = 12, D = 128, cut into 8 pieces per tile
+    n_q, n_k, H, D = 4680, 65520, 12, 128
+    say(f"case: KV-cache chunk n_q={n_q} n_k={n_k} H={H} D={D}, S=8")
+    xq = make_random(1, n_q, H, D, dtype="bf16", seed=12800, tangent_std=0.1)
+    xk = make_random(1, n_k, H, D, dtype="bf16", seed=12900, tangent_std=0.1)
+    x = dict(q=xq["q"], dq=xq["dq"], k=xk["k"], v=xk["v"], dk=xk["dk"], dv=xk["dv"])
+    mask = aj.attn_jvp_mask_rects(n_q, n_k, [0, n_q], [0, 1], [0], [n_k])
+    rows = np.array(sorted({0, 255, 256, 2047, n_q - 1} |
+                           set(np.random.default_rng(4).integers(0, n_q, 24).tolist())))
+    parity(x, rects_allowed(n_q, n_k, [(0, n_q, 0, n_k)]), mask, 8, "bf16", rows=rows)
+
+
+def test_auto_split_frame_against_long_prefix():
+    # few query tiles against many keys: the chooser cuts, results stay exact
+    n_q, n_k, H, D = 520, 6000, 2, 128
+    xq = make_random(1, n_q, H, D, dtype="bf16", seed=13000, tangent_std=0.1)
+    xk = make_random(1, n_k, H, D, dtype="bf16", seed=13001, tangent_std=0.1)
+    x = dict(q=xq["q"], dq=xq["dq"], k=xk["k"], v=xk["v"], dk=xk["dk"], dv=xk["dv"])
+    mask = aj.attn_jvp_mask_rects(n_q, n_k, [0, n_q], [0, 1], [0], [n_k])
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    S = aj.attn_jvp_split_choose(x["q"], x["k"], mask, n_cu)
+    say(f"case: auto split n_q={n_q} n_k={n_k}: {n_cu} compute units -> max_splits={S}")
+    assert S > 1
+    parity(x, rects_allowed(n_q, n_k, [(0, n_q, 0, n_k)]), mask, "auto", "bf16")

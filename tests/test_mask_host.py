@@ -293,3 +293,78 @@ def test_block_causal_errors():
     for args in [(0, 4), (4, 0), (-1, 3), (1 << 16, 1 << 15)]:
         with pytest.raises(aj.AttnJvpError):
             aj.attn_jvp_mask_block_causal(*args)
+
+
+# ------------------------------------------------ split-key unit lists ----
+
+def check_split(mask, BM, BN, S):
+    """The unit list of a split launch against the rule in the C header,
+    recomputed here from the (separately tested) tile schedule."""
+    s = aj.attn_jvp_mask_schedule(mask, BM, BN)
+    u = aj.attn_jvp_mask_split_schedule(mask, BM, BN, S)
+    toff = s["tile_offsets"]
+    counts = np.diff(toff)
+    L = max(1, -(-int(counts.max(initial=0)) // S))
+    offs, tiles, parts, nparts = [0], [], [], 0
+    for t, n in enumerate(counts):
+        k = max(1, -(-int(n) // L))
+        for j in range(k):
+            offs.append(int(toff[t]) + (int(n) * (j + 1)) // k)
+            tiles.append(t)
+            parts.append(nparts + j if k > 1 else -1)
+        if k > 1:
+            nparts += k
+    np.testing.assert_array_equal(u["unit_offsets"], offs)
+    np.testing.assert_array_equal(u["unit_tile"], tiles)
+    np.testing.assert_array_equal(u["unit_part"], parts)
+    assert u["n_parts"] == nparts
+    # every entry of every tile in exactly one unit, in order; no unit longer than L
+    ucount = np.diff(u["unit_offsets"])
+    assert ucount.max(initial=0) <= L and ucount.min(initial=0) >= 0
+    for t in range(len(counts)):
+        mine = np.nonzero(u["unit_tile"] == t)[0]
+        assert len(mine) >= 1 and np.all(np.diff(mine) == 1)
+        assert u["unit_offsets"][mine[0]] == toff[t] and u["unit_offsets"][mine[-1] + 1] == toff[t + 1]
+    order = u["unit_order"]
+    assert sorted(order.tolist()) == list(range(len(tiles)))
+    key = [(-ucount[x], x) for x in order]
+    assert key == sorted(key)
+    return u
+
+
+@pytest.mark.parametrize("S", [1, 2, 3, 8, 1000])
+@pytest.mark.parametrize("nf,tpf,fpc", [(4, 16, 1), (6, 23, 2), (9, 60, 3)])
+def test_split_units_follow_the_rule(nf, tpf, fpc, S):
+    m = aj.attn_jvp_mask_tf(nf, tpf, fpc)
+    for BM, BN in [(128, 32), (256, 32), (64, 32)]:
+        u = check_split(m, BM, BN, S)
+        if S == 1:   # one unit per tile, nothing to merge
+            assert u["n_parts"] == 0 and np.all(u["unit_tile"] == np.arange(len(u["unit_tile"])))
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_split_units_random_rects(seed):
+    rng = np.random.default_rng(100 + seed)
+    n_q, n_k = int(rng.integers(1, 700)), int(rng.integers(1, 900))
+    m = aj.attn_jvp_mask_rects(n_q, n_k, *random_rects(rng, n_q, n_k))
+    for S in (1, 2, 5):
+        check_split(m, 128, 32, S)
+
+
+def test_split_units_kv_cache_rectangle():
+    # one chunk of queries against a long key sequence: every tile has the
+    # same list, cut into exactly max_splits pieces
+    m = aj.attn_jvp_mask_rects(4680, 65520, [0, 4680], [0, 1], [0], [65520])
+    u = check_split(m, 256, 32, 8)
+    assert len(u["unit_tile"]) == 19 * 8 and u["n_parts"] == 19 * 8
+    # a tile without any admissible key stays one empty unit
+    m = aj.attn_jvp_mask_rects(600, 400, [0, 256, 600], [0, 0, 1], [0], [400])
+    u = check_split(m, 256, 32, 4)
+    assert np.diff(u["unit_offsets"])[0] == 0 and u["unit_part"][0] == -1
+
+
+def test_split_errors():
+    m = aj.attn_jvp_mask_tf(4, 16, 1)
+    for args in [(128, 32, 0), (128, 32, -3), (128, 48, 2), (0, 32, 2)]:
+        with pytest.raises(aj.AttnJvpError):
+            aj.attn_jvp_mask_split_schedule(m, *args)
