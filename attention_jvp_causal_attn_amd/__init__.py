@@ -357,8 +357,9 @@ def attn_jvp_bwd(q, k, v, o, g_o, lse, mask, scale=None, g_q=None, g_k=None, g_v
                  delta=None, stream=None):
     """Gradients of sum(g_o * O) w.r.t. q, k, v for O = masked attention(q, k, v).
 
-    q, o, g_o: [B, n_q, H, D]; k, v: [B, n_k, H, D] bf16 device tensors with
-    the layout rules of attn_jvp_fwd; o and lse are the forward's outputs.
+    q, o, g_o: [B, n_q, H, D]; k, v: [B, n_k, H, D] device tensors of one dtype
+    (bfloat16 or float32) with the layout rules of attn_jvp_fwd; o and lse are
+    the forward's outputs.
     Outputs (allocated when not given): g_q like q, g_k and g_v like k, and
     delta [B, H, n_q] fp32 (the row sums <g_o, o>).  Asynchronous on
     ``stream``.  Returns (g_q, g_k, g_v, delta).

@@ -458,11 +458,11 @@ extern "C" int attn_jvp_bwd(const attn_jvp_bwd_args *a, const attn_jvp_mask *m, 
       !a->delta)
     return ATTN_JVP_ERR_NULL;
   if (a->B <= 0 || a->H <= 0 || a->n_q <= 0 || a->n_k <= 0) return ATTN_JVP_ERR_SHAPE;
-  if (a->dtype != ATTN_JVP_BF16 || (a->D != 64 && a->D != 128)) return ATTN_JVP_ERR_UNSUPPORTED;
+  if (a->D != 64 && a->D != 128) return ATTN_JVP_ERR_UNSUPPORTED;
   if (a->n_q != m->n_q || a->n_k != m->n_k) return ATTN_JVP_ERR_MASK;
   if (!(std::isfinite(a->scale))) return ATTN_JVP_ERR_SHAPE;
   if (int64_t(a->B) * a->H * std::max(a->n_q, a->n_k) > (int64_t(1) << 40)) return ATTN_JVP_ERR_SHAPE;
-  const int64_t es = 2;
+  const int64_t es = a->dtype == ATTN_JVP_BF16 ? 2 : 4;
   const int64_t qs[3] = {a->q_stride_b, a->q_stride_n, a->q_stride_h};
   const int64_t ks[3] = {a->k_stride_b, a->k_stride_n, a->k_stride_h};
   for (int i = 0; i < 3; ++i) {
@@ -488,8 +488,10 @@ extern "C" int attn_jvp_bwd(const attn_jvp_bwd_args *a, const attn_jvp_mask *m, 
 
   int device = -1;
   if (hipGetDevice(&device) != hipSuccess) return ATTN_JVP_ERR_HIP;
-  const int BM = a->D == 128 ? attnjvp::kBwdBlockMWide : attnjvp::kBwdBlockM;
-  const int BN = attnjvp::kBwdBlockN;
+  const bool bf16 = a->dtype == ATTN_JVP_BF16;
+  const int BM = !bf16 ? attnjvp::kF32BlockM
+                       : (a->D == 128 ? attnjvp::kBwdBlockMWide : attnjvp::kBwdBlockM);
+  const int BN = bf16 ? attnjvp::kBwdBlockN : attnjvp::kF32BlockN;
   const DeviceSchedule *rs = nullptr, *cs = nullptr;
   const attn_jvp_mask *t = nullptr;
   {
@@ -528,7 +530,8 @@ extern "C" int attn_jvp_bwd(const attn_jvp_bwd_args *a, const attn_jvp_mask *m, 
   p.c_offsets = cs->tile_offsets; p.c_order = cs->tile_order; p.c_entries = cs->entries;
   p.c_bits = cs->partial_bits; p.c_partial = cs->n_partial;
   p.c_map = make_work_map(slices, cs->n_tiles);
-  const int err = a->D == 128 ? attnjvp::launch_bwd_bf16_wide(p, stream)
+  const int err = !bf16 ? attnjvp::launch_bwd_f32(p, a->D, stream)
+                 : a->D == 128 ? attnjvp::launch_bwd_bf16_wide(p, stream)
                                : attnjvp::launch_bwd_bf16(p, a->D, stream);
   return err == hipSuccess ? ATTN_JVP_OK : ATTN_JVP_ERR_HIP;
 }

@@ -222,6 +222,7 @@ int launch_bf16(const KernelParams &p, int D, bool tangent, void *stream);
 int launch_bf16_wide(const KernelParams &p, bool tangent, void *stream);  // D = 128
 int launch_bwd_bf16(const BwdParams &p, int D, void *stream);
 int launch_bwd_bf16_wide(const BwdParams &p, void *stream);  // D = 128
+int launch_bwd_f32(const BwdParams &p, int D, void *stream);
 int launch_f32(const KernelParams &p, int D, bool tangent, void *stream);
 int launch_merge(const MergeParams &p, int D, bool bf16, bool tangent, void *stream);
 

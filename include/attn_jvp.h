@@ -254,7 +254,8 @@ int attn_jvp_split_choose(const attn_jvp_args *a, const attn_jvp_mask *m,
  * the forward's) and delta (output) are [B, H, n_q] fp32, contiguous.  delta
  * receives D_i = <g_o_i, O_i>, the row sums the pass needs; it is returned so
  * the caller owns all memory.  Every pointer and stride in bytes a multiple
- * of 16; outputs alias nothing.  Supported: dtype ATTN_JVP_BF16, D = 64 or 128. */
+ * of 16; outputs alias nothing.  Supported: both dtypes (bf16: MFMA products,
+ * fp32 accumulation, bf16 outputs; fp32: fp32 throughout), D = 64 or 128. */
 typedef struct attn_jvp_bwd_args {
   int32_t dtype;
   int32_t B, H;
@@ -275,8 +276,8 @@ typedef struct attn_jvp_bwd_args {
  * writes delta) then a dK/dV pass over key tiles of the transposed mask
  * (built and uploaded on first use, cached with the mask).  Asynchronous,
  * deterministic (no atomics).  Errors: ERR_NULL, ERR_DTYPE, ERR_SHAPE,
- * ERR_ALIGN, ERR_MASK, ERR_UNSUPPORTED (dtype other than bf16, D other than
- * 64 or 128, aliasing), ERR_HIP, ERR_OOM. */
+ * ERR_ALIGN, ERR_MASK, ERR_UNSUPPORTED (D other than 64 or 128, aliasing),
+ * ERR_HIP, ERR_OOM. */
 int attn_jvp_bwd(const attn_jvp_bwd_args *a, const attn_jvp_mask *m,
                  void *hip_stream);
 

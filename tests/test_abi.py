@@ -199,8 +199,8 @@ BAD_BWD = [
     (dict(lse=None), _lib.ATTN_JVP_ERR_NULL),
     (dict(delta=None), _lib.ATTN_JVP_ERR_NULL),
     (dict(g_v=None), _lib.ATTN_JVP_ERR_NULL),
-    (dict(dtype=1), _lib.ATTN_JVP_ERR_UNSUPPORTED),
     (dict(D=96), _lib.ATTN_JVP_ERR_UNSUPPORTED),
+    (dict(dtype=1, k_stride_n=258), _lib.ATTN_JVP_ERR_ALIGN),   # fp32: 1032-byte rows
     (dict(B=0), _lib.ATTN_JVP_ERR_SHAPE),
     (dict(n_k=11), _lib.ATTN_JVP_ERR_MASK),
     (dict(g_q=0x70008), _lib.ATTN_JVP_ERR_ALIGN),
@@ -222,8 +222,9 @@ def test_bwd_rejects_bad_arguments(kw, status):
 @pytest.mark.skipif(_gpu_present(), reason="needs a host without a HIP device")
 def test_bwd_without_device_reports_hip_error():
     mask = aj.attn_jvp_mask_tf(4, 16, 1)
-    a = _bwd_args(mask)
-    assert _lib.lib().attn_jvp_bwd(ctypes.byref(a), mask.handle, None) == _lib.ATTN_JVP_ERR_HIP
+    for dtype in (0, 1):
+        a = _bwd_args(mask, dtype=dtype)
+        assert _lib.lib().attn_jvp_bwd(ctypes.byref(a), mask.handle, None) == _lib.ATTN_JVP_ERR_HIP
 
 
 def test_split_choose():
