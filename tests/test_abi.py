@@ -250,3 +250,22 @@ def test_split_choose():
     assert L.attn_jvp_split_choose(ctypes.byref(a), m.handle, 256, None) == _lib.ATTN_JVP_ERR_NULL
     assert L.attn_jvp_split_choose(ctypes.byref(_args(m, n_q=1560, n_k=32760, D=96)), m.handle,
                                    256, ctypes.byref(out)) == _lib.ATTN_JVP_ERR_UNSUPPORTED
+
+
+def test_plain_c_caller(tmp_path):
+    """The header compiles as C99 and a C program linked against the library
+    exercises the host-side entry points (no GPU needed)."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    src = os.path.join(ROOT, "tests", "c_abi", "host_calls.c")
+    exe = str(tmp_path / "host_calls")
+    libdir = os.path.dirname(_lib.LIB_PATH)
+    r = subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-I",
+                        os.path.join(ROOT, "include"), src, "-o", exe, "-L", libdir,
+                        "-lattn_jvp", f"-Wl,-rpath,{libdir}"], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0 and r.stdout.strip() == "ok", r.stdout + r.stderr
