@@ -214,8 +214,9 @@ static int validate_fwd(const attn_jvp_args *a, const attn_jvp_mask *m, bool *ta
     if (qs[i] < 0 || ks[i] < 0) return ATTN_JVP_ERR_SHAPE;
     if ((qs[i] * es) % 16 || (ks[i] * es) % 16) return ATTN_JVP_ERR_ALIGN;
   }
-  // the kernels address a 32-key block with 32-bit byte offsets
-  if (ks[1] * es * 32 > int64_t(0x7fffffff)) return ATTN_JVP_ERR_SHAPE;
+  // the kernels address a 32-row block with 32-bit byte offsets
+  if (ks[1] * es * 32 > int64_t(0x7fffffff) || qs[1] * es * 32 > int64_t(0x7fffffff))
+    return ATTN_JVP_ERR_SHAPE;
   // rows of one head must not overlap the D contiguous elements of another
   if (a->H > 1 && (qs[2] < a->D || ks[2] < a->D)) return ATTN_JVP_ERR_SHAPE;
   const void *ins[6] = {a->q, a->k, a->v, a->dq, a->dk, a->dv};

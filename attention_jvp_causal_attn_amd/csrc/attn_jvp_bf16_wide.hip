@@ -366,11 +366,17 @@ void attn_jvp_bf16_wide_kernel(KernelParams p) {
                          : static_cast<const void *>(static_cast<const __bf16 *>(p.dq) + qoff);
 #pragma unroll
     for (int i = 0; i < BM * KCH / kThreads; ++i) {
+      // 32 rows per step: a 64-bit base at the step's first (clamped) row,
+      // 32-bit lane offsets inside it
       const int q = i * kThreads + threadIdx.x;
       const int row = q / KCH, pch = q % KCH;
+      const int rb = min(tile * BM + i * (kThreads / KCH), p.n_q - 1);
       const int grow = min(tile * BM + row, p.n_q - 1);
-      const uint32_t roff = zq ? 0u : uint32_t(grow) * uint32_t(p.q_sn) * 2u;
-      dma16(dqb, roff + uint32_t(pch ^ k_swz(row)) * 16u,
+      const void *src = zq ? dqb
+                           : static_cast<const void *>(static_cast<const __bf16 *>(dqb) +
+                                                       int64_t(rb) * p.q_sn);
+      const uint32_t roff = zq ? 0u : uint32_t(grow - rb) * uint32_t(p.q_sn) * 2u;
+      dma16(src, roff + uint32_t(pch ^ k_swz(row)) * 16u,
             dq_base + uint32_t(i * kThreads + wave * 64) * 16u);
     }
   }

@@ -342,10 +342,14 @@ void bwd_dkv_wide_kernel(BwdParams p) {
     const __bf16 *vb = static_cast<const __bf16 *>(p.v) + koff;
 #pragma unroll
     for (int i = 0; i < BM * KCH / kThreads; ++i) {
+      // 32 rows per step: a 64-bit base at the step's first (clamped) row,
+      // 32-bit lane offsets inside it
       const int q = i * kThreads + threadIdx.x;
       const int row = q / KCH, pch = q % KCH;
+      const int rb = min(tile * BM + i * (kThreads / KCH), p.n_k - 1);
       const int grow = min(tile * BM + row, p.n_k - 1);
-      dma16(vb, uint32_t(grow) * uint32_t(p.k_sn) * 2u + uint32_t(pch ^ sw(row)) * 16u,
+      dma16(vb + int64_t(rb) * p.k_sn,
+            uint32_t(grow - rb) * uint32_t(p.k_sn) * 2u + uint32_t(pch ^ sw(row)) * 16u,
             v_base + uint32_t(i * kThreads + wave * 64) * 16u);
     }
   }

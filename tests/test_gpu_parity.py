@@ -413,3 +413,43 @@ def test_full_size_workload_sampled(wid):
     rows = sample_rows(w, seed=wid)
     say(f"  {len(rows)} sampled rows per (b, h)")
     parity(x, pred, mask, TOL[torch.bfloat16], rows=rows)
+
+
+def test_rows_beyond_4gib_of_one_slice():
+    # A (batch, head) slice whose rows span more than 4 GiB (row stride 2^20
+    # elements, 2,100 rows): the tile staging must not wrap 32-bit byte
+    # offsets.  Forward (dQ tile staging) and backward (V tile staging of the
+    # dK/dV pass), checked against the oracle.
+    from oracle import masked_attention_grad
+    nf, tpf, D, SN = 7, 150, 128, 1 << 20
+    pred = tf_allowed(nf, tpf, 1)
+    N = pred.n_q
+    assert (N - 1) * SN * 2 > (1 << 32)
+    say(f"case: bf16 TF N={N} D={D}, row stride {SN} elements ({N * SN * 2 / 2**30:.1f} GiB per tensor)")
+    x = make_random(1, N, 1, D, dtype="bf16", seed=9990, tangent_std=0.1)
+    g = make_random(1, N, 1, D, dtype="bf16", seed=9991)["q"]
+
+    def big(src=None):
+        buf = torch.empty((N, SN), dtype=torch.bfloat16, device=DEV)
+        v = buf[:, :D].unsqueeze(0).unsqueeze(2)          # [1, N, 1, D], strides (.., SN, .., 1)
+        if src is not None:
+            v.copy_(src.to(DEV))
+        return v
+
+    t = {n: big(x[n]) for n in ("q", "k", "v", "dq", "dk", "dv")}
+    o, do, gq, gk, gv, gd = big(), big(), big(), big(), big(), big(g)
+    mask = aj.attn_jvp_mask_tf(nf, tpf, 1)
+    lse = torch.empty(1, 1, N, dtype=torch.float32, device=DEV)
+    aj.attn_jvp_fwd(t["q"], t["k"], t["v"], t["dq"], t["dk"], t["dv"], mask, o=o, d_o=do, lse=lse)
+    torch.cuda.synchronize()
+    O, dO, LSE = masked_attention_jvp(x["q"], x["k"], x["v"], x["dq"], x["dk"], x["dv"], pred)
+    check("O", f64(o), O, 2e-2)
+    check("dO", f64(do), dO, 2e-2)
+    check("LSE", f64(lse), LSE, 2e-2)
+    po, _, plse = aj.attn_jvp_fwd(t["q"], t["k"], t["v"], None, None, None, mask, o=o, lse=lse)
+    aj.attn_jvp_bwd(t["q"], t["k"], t["v"], po, gd, plse, mask, g_q=gq, g_k=gk, g_v=gv)
+    torch.cuda.synchronize()
+    dQ, dK, dV, _ = masked_attention_grad(x["q"], x["k"], x["v"], g, pred)
+    check("dQ", f64(gq), dQ, 2e-2)
+    check("dK", f64(gk), dK, 2e-2)
+    check("dV", f64(gv), dV, 2e-2)
