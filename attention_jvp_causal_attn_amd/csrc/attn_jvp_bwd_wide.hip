@@ -231,7 +231,7 @@ void bwd_dq_wide_kernel(BwdParams p) {
     for (int t = 0; t < KSTEPS; ++t) {
       S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand(st->k, krow, t, hh), qf[t], S, 0, 0, 0);
       G = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand(st->v, krow, t, hh), gf[t], G, 0, 0, 0);
-      if (t % 2 == 1) __builtin_amdgcn_sched_barrier(0);  // bound the operand prefetch
+      if (t % 4 == 3) __builtin_amdgcn_sched_barrier(0);  // bound the operand prefetch
     }
     if (j + 1 < n) issue((j + 1) & 1, entry(j + 1));  // its stage was released by the barrier
     const uint32_t bits = ent.y >= 0 ? st->bits[row_in_tile] >> (8 * hh) : ~0u;
@@ -252,7 +252,7 @@ void bwd_dq_wide_kernel(BwdParams p) {
       for (int nt = 0; nt < DT; ++nt) {
         acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(st->k, s, nt, tl.dcol, tl.krel),
                                                           gsb[s], acc[nt], 0, 0, 0);
-        if (nt % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+        if (nt % 4 == 3) __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
@@ -385,7 +385,7 @@ void bwd_dkv_wide_kernel(BwdParams p) {
       const bf16x8 vf = as_bf16x8(vrow[(2 * t + hh) ^ sw(key_in_tile)]);
       S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand(st->q, qperm, t, hh), kf[t], S, 0, 0, 0);
       G = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand(st->g, qperm, t, hh), vf, G, 0, 0, 0);
-      if (t % 2 == 1) __builtin_amdgcn_sched_barrier(0);  // bound the operand prefetch
+      if (t % 4 == 3) __builtin_amdgcn_sched_barrier(0);  // bound the operand prefetch
     }
     if (j + 1 < n) issue((j + 1) & 1, entry(j + 1));  // its stage was released by the barrier
     // LSE and D of this lane's 16 queries 8hh + {0..7} and 16 + 8hh + {0..7}:
@@ -427,7 +427,7 @@ void bwd_dkv_wide_kernel(BwdParams p) {
                                                            pb[s], accV[nt], 0, 0, 0);
         accK[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(st->q, s, nt, tl.dcol, tl.krel),
                                                            gsb[s], accK[nt], 0, 0, 0);
-        if (nt % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+        if (nt % 4 == 3) __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
