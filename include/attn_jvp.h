@@ -202,7 +202,9 @@ typedef struct attn_jvp_args {
  * ERR_HIP; faults inside the kernel surface at the caller's next
  * synchronisation.  The first call for a (mask, device, tile shape) builds and
  * uploads the tile schedule (a blocking device allocation and copy); later
- * calls launch only.  Deterministic: no atomics, fixed reduction order.
+ * calls launch only, so they can be captured into a HIP graph (the same holds
+ * for attn_jvp_fwd_split and attn_jvp_bwd once their schedules are uploaded).
+ * Deterministic: no atomics, fixed reduction order.
  * Errors: ERR_NULL, ERR_DTYPE, ERR_SHAPE, ERR_ALIGN, ERR_MASK (mask sizes
  * differ from n_q/n_k), ERR_UNSUPPORTED, ERR_HIP, ERR_OOM. */
 int attn_jvp_fwd(const attn_jvp_args *a, const attn_jvp_mask *m,
