@@ -13,7 +13,12 @@
  *   s_j = scale <q_i,k_j>,  p = softmax_{J_i}(s),  O_i = sum_j p_j v_j,
  *   LSE_i = ln sum_{j in J_i} exp(s_j),
  *   ds_j = scale (<dq_i,k_j> + <q_i,dk_j>),  mu_i = sum_j p_j ds_j,
- *   dO_i = sum_j p_j (ds_j - mu_i) v_j + sum_j p_j dv_j.
+ *   dO_i = sum_j p_j (ds_j - mu_i) v_j + sum_j p_j dv_j,
+ *   dLSE_i = mu_i (the tangent of LSE, an optional output).
+ *
+ * Around it: a split-key variant of the same pass (attn_jvp_fwd_split) and
+ * the backward of the primal, the gradients of sum(g * O) with respect to Q,
+ * K and V reusing the forward's LSE (attn_jvp_bwd).
  *
  * Masks are query groups with admissible key ranges (Appendix B: custom masks
  * as query-key rectangles, one sparse schedule shared by the primal and the
@@ -49,7 +54,8 @@ enum attn_jvp_status {
   ATTN_JVP_ERR_MASK = -5,        /* malformed mask description, or mask size
                                     differs from the tensors */
   ATTN_JVP_ERR_UNSUPPORTED = -6, /* valid but not implemented (head dim,
-                                    aliasing outputs) */
+                                    aliasing outputs, the LSE tangent
+                                    without any input tangent) */
   ATTN_JVP_ERR_HIP = -7,         /* no usable HIP device, or a HIP call failed */
   ATTN_JVP_ERR_OOM = -8          /* host or device allocation failed */
 };
