@@ -453,3 +453,39 @@ def test_rows_beyond_4gib_of_one_slice():
     check("dQ", f64(gq), dQ, 2e-2)
     check("dK", f64(gk), dK, 2e-2)
     check("dV", f64(gv), dV, 2e-2)
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("bf16", 64), ("f32", 64)])
+def test_head_major_memory_layout(dtype, D):
+    # tensors stored [B, H, N, D] (row stride D, head stride N * D) and passed
+    # as [B, N, H, D] views: forward, split forward and backward
+    from oracle import masked_attention_grad
+    pred = tf_allowed(5, 37, 1)
+    B, H, N = 2, 3, pred.n_q
+    say(f"case: head-major layout {dtype} D={D} B={B} H={H} N={N}")
+    x = make_random(B, N, H, D, dtype=dtype, seed=13200 + D, tangent_std=0.1)
+    hm = {k: v.permute(0, 2, 1, 3).contiguous().to(DEV).permute(0, 2, 1, 3) for k, v in x.items()}
+    assert hm["q"].stride(1) == D and hm["q"].stride(2) == N * D
+    mask = aj.attn_jvp_mask_tf(5, 37, 1)
+    out = lambda: torch.empty(B, H, N, D, dtype=hm["q"].dtype, device=DEV).permute(0, 2, 1, 3)
+    tol = TOL[hm["q"].dtype]
+    O, dO, LSE = masked_attention_jvp(x["q"], x["k"], x["v"], x["dq"], x["dk"], x["dv"], pred)
+    for S in (1, 3):
+        o, do = out(), out()
+        _, _, lse = aj.attn_jvp_fwd(hm["q"], hm["k"], hm["v"], hm["dq"], hm["dk"], hm["dv"], mask,
+                                    o=o, d_o=do, max_splits=S)
+        torch.cuda.synchronize()
+        check(f"O (S={S})", f64(o), O, tol)
+        check(f"dO (S={S})", f64(do), dO, tol)
+        check(f"LSE (S={S})", f64(lse), LSE, tol)
+    g = make_random(B, N, H, D, dtype=dtype, seed=13300 + D)["q"]
+    gd = g.permute(0, 2, 1, 3).contiguous().to(DEV).permute(0, 2, 1, 3)
+    o = out()
+    _, _, lse = aj.attn_jvp_fwd(hm["q"], hm["k"], hm["v"], None, None, None, mask, o=o)
+    gq, gk, gv = out(), out(), out()
+    aj.attn_jvp_bwd(hm["q"], hm["k"], hm["v"], o, gd, lse, mask, g_q=gq, g_k=gk, g_v=gv)
+    torch.cuda.synchronize()
+    dQ, dK, dV, _ = masked_attention_grad(x["q"], x["k"], x["v"], g, pred)
+    check("dQ", f64(gq), dQ, tol)
+    check("dK", f64(gk), dK, tol)
+    check("dV", f64(gv), dV, tol)
