@@ -165,7 +165,7 @@ extern "C" int attn_jvp_tile_shape(int32_t dtype, int32_t D, int32_t *block_m, i
   if (dtype != ATTN_JVP_BF16 && dtype != ATTN_JVP_F32) return ATTN_JVP_ERR_DTYPE;
   if (D != 64 && D != 128) return ATTN_JVP_ERR_UNSUPPORTED;
   if (dtype == ATTN_JVP_BF16) {
-    *block_m = D == 128 ? attnjvp::kBf16BlockMWide : attnjvp::kBf16BlockM;
+    *block_m = attnjvp::kBf16BlockMWide;
     *block_n = attnjvp::kBf16BlockN;
   } else {
     *block_m = attnjvp::kF32BlockM;

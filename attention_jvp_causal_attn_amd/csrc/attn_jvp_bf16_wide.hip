@@ -1,4 +1,4 @@
-// Fused primal + tangent masked attention for gfx950, head dim 128
+// Fused primal + tangent masked attention for gfx950, head dims 64 and 128
 // (bf16 in, fp32 accumulate).
 //
 // One online-softmax pass computes O, LSE and dO ("Causal-rCM ..." summary,
@@ -31,10 +31,12 @@
 //    ds_read_b64_tr_b16 (each group of 16 lanes turns 4 keys x 16 dims into
 //    16 lanes x 4 keys);
 //  * key blocks of 32 rows of K, dK, V, dV (and the admissible-key bits of
-//    the block) go HBM -> LDS with direct-to-LDS loads, one 16-byte chunk per
-//    lane per tensor, into a 2-stage ring: block j + 1 is copied while block
-//    j is computed; tiles are XOR-swizzled in 16-byte chunks so the operand
-//    reads hit distinct banks;
+//    the block) go HBM -> LDS with direct-to-LDS loads, 16 bytes per lane per
+//    copy, into a 2-stage ring: block j + 1 is copied while block j is
+//    computed; tiles are XOR-swizzled in 16-byte chunks so the operand reads
+//    hit distinct banks;
+//  * head dim 64 runs the same code with half the k-steps and output tiles
+//    (and 128-byte rows: other swizzles, two tensors per copy round);
 //  * every value lives in the 256 VGPRs a wave has at two waves per SIMD
 //    (accumulators included, so the rare rescale is plain vector code); the
 //    reference max moves only when a row max exceeds it by more than 2^8, so
@@ -60,15 +62,11 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int D = 128;
 constexpr int kThreads = 512;
 constexpr int kWaves = 8;
 constexpr int BM = kBf16BlockMWide;  // 256 query rows per workgroup
 constexpr int BN = kBf16BlockN;      // 32 keys per block
 constexpr int kStages = 2;
-constexpr int KCH = D / 8;           // 16-byte chunks per row
-constexpr int KSTEPS = D / 16;
-constexpr int DT = D / 32;
 static_assert(BM == 32 * kWaves && BN == 32, "one wave per 32 rows, 32-key blocks");
 
 constexpr float kNegInf = -__builtin_inff();
@@ -76,11 +74,22 @@ constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kRescaleSlack = 8.0f;  // log2 units: p <= 2^8 between rescales
 constexpr int kEntChunk = 512;        // schedule entries staged in LDS at a time
 
+// Per head dim: 16-byte chunks per row, 16-wide k-steps, 32-wide output tiles.
+template <int D>
+struct Geo {
+  static_assert(D == 64 || D == 128, "head dim 64 or 128");
+  static constexpr int KCH = D / 8;
+  static constexpr int KSTEPS = D / 16;
+  static constexpr int DT = D / 32;
+  static constexpr int TILE = BN * KCH;  // chunks of one 32-row tile
+};
+
+template <int D>
 struct alignas(16) StageTile {
-  uint4 k[BN * KCH];
-  uint4 dk[BN * KCH];
-  uint4 v[BN * KCH];
-  uint4 dv[BN * KCH];
+  uint4 k[Geo<D>::TILE];
+  uint4 dk[Geo<D>::TILE];
+  uint4 v[Geo<D>::TILE];
+  uint4 dv[Geo<D>::TILE];
   uint32_t bits[BM];
 };
 
@@ -91,9 +100,17 @@ __device__ __forceinline__ int swap_bits23(int m) {
   return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
 }
 // 16-byte-chunk XOR swizzles: row-operand reads (K, dK, dQ) touch 16 rows at
-// one chunk; transposed reads (V, dV) touch 4 rows x 4 chunks.
-__device__ __forceinline__ int k_swz(int row) { return row & 15; }
-__device__ __forceinline__ int v_swz(int row) { return 4 * (row & 3); }
+// one chunk; transposed reads (V, dV) touch 4 rows x 4 chunks.  Head dim 128
+// (256-byte rows): one swizzle for each access; head dim 64 (128-byte rows):
+// one swizzle conflict-free for both.
+template <int D>
+__device__ __forceinline__ int k_swz(int row) {
+  return D == 128 ? (row & 15) : (2 * ((row >> 1) & 3) | ((row >> 3) & 1));
+}
+template <int D>
+__device__ __forceinline__ int v_swz(int row) {
+  return D == 128 ? 4 * (row & 3) : (2 * ((row >> 1) & 3) | ((row >> 3) & 1));
+}
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 x) { return __builtin_bit_cast(bf16x8, x); }
 
@@ -128,66 +145,96 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 // A zero row: the copy source of an absent (zero) tangent tensor, read with
 // row-independent offsets.
-__device__ __align__(16) uint4 kZeroRow[KCH];
+__device__ __align__(16) uint4 kZeroRow[16];
 
-// One 16-byte chunk per lane per tensor: 512 lanes cover a 32 x 128 tile.
-static_assert(BN * KCH == kThreads, "one chunk per lane per tensor tile");
-
-// Per-lane byte offsets inside a key block (K-swizzled, V-swizzled).
+// Per-lane byte offsets of chunk c of a 32-row tile (K-swizzled, V-swizzled).
 struct DmaOffsets {
   uint32_t k, v;
 };
-__device__ __forceinline__ DmaOffsets dma_offsets(int64_t k_sn, int rows_valid) {
-  const int q = threadIdx.x;
-  const int row = q / KCH, pch = q % KCH;
+template <int D>
+__device__ __forceinline__ DmaOffsets dma_offsets(int c, int64_t k_sn, int rows_valid) {
+  constexpr int KCH = Geo<D>::KCH;
+  const int row = c / KCH, pch = c % KCH;
   const uint32_t roff = uint32_t(min(row, rows_valid - 1)) * uint32_t(k_sn) * 2u;
-  return {roff + uint32_t(pch ^ k_swz(row)) * 16u, roff + uint32_t(pch ^ v_swz(row)) * 16u};
+  return {roff + uint32_t(pch ^ k_swz<D>(row)) * 16u, roff + uint32_t(pch ^ v_swz<D>(row)) * 16u};
 }
 
 // Issue the direct-to-LDS copies of the key block starting at key key0 into
-// the stage tile at LDS byte address st.
-template <bool TAN>
+// the stage tile at LDS byte address st.  The block's tensors (K, V, then dK,
+// dV) are consecutive runs of Geo<D>::TILE chunks; copy i of wave w fills the
+// 64 chunks from i * 512 + 64 w, which lie inside one tensor (head dim 128:
+// one copy per tensor per wave; head dim 64: waves 0-3 and 4-7 take the two
+// tensors of a pair).
+template <int D, bool TAN>
 __device__ __forceinline__ void issue_block(uint32_t st, int wave, const KernelParams &p,
                                             const __bf16 *kb_, const __bf16 *dkb_,
                                             const __bf16 *vb_, const __bf16 *dvb_, int key0,
                                             const uint32_t *bits_src) {
+  using ST = StageTile<D>;
+  constexpr int TILE = Geo<D>::TILE;
+  constexpr int COPIES = (TAN ? 4 : 2) * TILE / kThreads;
   const int lane = threadIdx.x & 63;
   const int64_t boff = int64_t(key0) * p.k_sn;
   // rebuilt per block (cheaper than holding them in registers); rows past n_k
   // re-read the last key, masked out by the schedule
-  const DmaOffsets o = dma_offsets(p.k_sn, min(BN, p.n_k - key0));
-  const uint32_t chunk = uint32_t(wave * 64) * 16u;
-  dma16(kb_ + boff, o.k, st + uint32_t(offsetof(StageTile, k)) + chunk);
-  dma16(vb_ + boff, o.v, st + uint32_t(offsetof(StageTile, v)) + chunk);
-  if (TAN) {
-    // an absent tangent tensor is zero: copy the zero row into every row
-    const DmaOffsets oz = dma_offsets(0, 1);
-    const bool zk = dkb_ == nullptr, zv = dvb_ == nullptr;
-    dma16(zk ? static_cast<const void *>(kZeroRow) : dkb_ + boff, zk ? oz.k : o.k,
-          st + uint32_t(offsetof(StageTile, dk)) + chunk);
-    dma16(zv ? static_cast<const void *>(kZeroRow) : dvb_ + boff, zv ? oz.v : o.v,
-          st + uint32_t(offsetof(StageTile, dv)) + chunk);
+  const int rows_valid = min(BN, p.n_k - key0);
+  if constexpr (D == 128) {
+    // one copy per tensor per wave, all at this lane's chunk: one offset pair
+    // serves the four tensors (the general loop below compiles slower here)
+    const DmaOffsets o = dma_offsets<D>(int(threadIdx.x), p.k_sn, rows_valid);
+    const uint32_t chunk = uint32_t(wave * 64) * 16u;
+    dma16(kb_ + boff, o.k, st + uint32_t(offsetof(ST, k)) + chunk);
+    dma16(vb_ + boff, o.v, st + uint32_t(offsetof(ST, v)) + chunk);
+    if (TAN) {
+      // an absent tangent tensor is zero: copy the zero row into every row
+      const DmaOffsets oz = dma_offsets<D>(int(threadIdx.x), 0, 1);
+      const bool zk = dkb_ == nullptr, zv = dvb_ == nullptr;
+      dma16(zk ? static_cast<const void *>(kZeroRow) : dkb_ + boff, zk ? oz.k : o.k,
+            st + uint32_t(offsetof(ST, dk)) + chunk);
+      dma16(zv ? static_cast<const void *>(kZeroRow) : dvb_ + boff, zv ? oz.v : o.v,
+            st + uint32_t(offsetof(ST, dv)) + chunk);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < COPIES; ++i) {
+      const int c0 = i * kThreads + wave * 64;  // wave-uniform
+      const int t = c0 / TILE;                  // 0 K, 1 V, 2 dK, 3 dV
+      const int c = c0 % TILE + lane;
+      const uint32_t dst = st + uint32_t(c0 % TILE) * 16u +
+                           uint32_t(t == 0 ? offsetof(ST, k) : t == 1 ? offsetof(ST, v)
+                                    : t == 2 ? offsetof(ST, dk) : offsetof(ST, dv));
+      // an absent tangent tensor is zero: copy the zero row into every row
+      const __bf16 *src = t == 0 ? kb_ : t == 1 ? vb_ : t == 2 ? dkb_ : dvb_;
+      if (src == nullptr) {
+        const DmaOffsets oz = dma_offsets<D>(c, 0, 1);
+        dma16(kZeroRow, (t & 1) ? oz.v : oz.k, dst);
+      } else {
+        const DmaOffsets o = dma_offsets<D>(c, p.k_sn, rows_valid);
+        dma16(src + boff, (t & 1) ? o.v : o.k, dst);
+      }
+    }
   }
   // mask bits: BM words = 64 chunks; wave w copies chunks 8w .. 8w+7 (lanes 0..7)
   if (lane < 8)
     dma16(bits_src, uint32_t(wave * 8 + lane) * 16u,
-          st + uint32_t(offsetof(StageTile, bits)) + uint32_t(wave) * 128u);
+          st + uint32_t(offsetof(StageTile<D>, bits)) + uint32_t(wave) * 128u);
 }
 
 // S^T = K Q^T and dS^T = K dQ^T + dK Q^T; Q from registers, dQ from LDS.
-template <bool TAN>
-__device__ __forceinline__ void score_block(const StageTile *st, const uint4 *dq_lds,
+template <int D, bool TAN>
+__device__ __forceinline__ void score_block(const StageTile<D> *st, const uint4 *dq_lds,
                                             const bf16x8 *qf, int row_in_tile, f32x16 &S,
                                             f32x16 &dS) {
   const int lane = threadIdx.x & 63;
   const int col = lane & 31, hh = lane >> 5;
   const int krow = swap_bits23(col);
+  constexpr int KCH = Geo<D>::KCH, KSTEPS = Geo<D>::KSTEPS;
   const uint4 *Ks = st->k + krow * KCH;
   const uint4 *dKs = st->dk + krow * KCH;
   const uint4 *dQs = dq_lds + row_in_tile * KCH;
   // opaque per call: the per-step addresses are rebuilt each block instead of
   // being held in registers across the key loop
-  int kx = k_swz(krow), qx = k_swz(row_in_tile);
+  int kx = k_swz<D>(krow), qx = k_swz<D>(row_in_tile);
   asm volatile("" : "+v"(kx), "+v"(qx));
   S = f32x16{};
   dS = f32x16{};
@@ -208,12 +255,13 @@ __device__ __forceinline__ void score_block(const StageTile *st, const uint4 *dq
 }
 
 // Masking, online-softmax update and value step of one key block.
-template <bool TAN>
-__device__ __forceinline__ void softmax_value_block(const StageTile *st, f32x16 S, f32x16 dS,
+template <int D, bool TAN>
+__device__ __forceinline__ void softmax_value_block(const StageTile<D> *st, f32x16 S, f32x16 dS,
                                                     f32x16 *accO, f32x16 *accT, float &m_ref,
                                                     float &l_run, float &mu_run, bool partial,
                                                     int row_in_tile, float scale_log2,
                                                     float scale) {
+  constexpr int KCH = Geo<D>::KCH, DT = Geo<D>::DT;
   const int lane = threadIdx.x & 63;
   const int hh = lane >> 5;
   if (partial) {
@@ -282,7 +330,7 @@ __device__ __forceinline__ void softmax_value_block(const StageTile *st, f32x16 
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const int key = 16 * s + 4 * half + krel;
-        const int chunk = key * KCH + ((d >> 3) ^ v_swz(key));
+        const int chunk = key * KCH + ((d >> 3) ^ v_swz<D>(key));
         const char *vp = reinterpret_cast<const char *>(st->v + chunk) + (d & 7) * 2;
         vh[half] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
             (__attribute__((address_space(3))) bf16x4 *)(vp));
@@ -304,10 +352,12 @@ __device__ __forceinline__ void softmax_value_block(const StageTile *st, f32x16 
   }
 }
 
-template <bool TAN>
+template <int D, bool TAN>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_jvp_bf16_wide_kernel(KernelParams p) {
-  __shared__ StageTile ring[kStages];
+  constexpr int KCH = Geo<D>::KCH, KSTEPS = Geo<D>::KSTEPS, DT = Geo<D>::DT;
+  using Stage = StageTile<D>;
+  __shared__ Stage ring[kStages];
   __shared__ uint4 dq_lds[TAN ? BM * KCH : 1];
   __shared__ int2 ents[2][kEntChunk];
 
@@ -323,7 +373,7 @@ void attn_jvp_bf16_wide_kernel(KernelParams p) {
   const int col = lane & 31, hh = lane >> 5;
   const int row_in_tile = wave * 32 + col;
   const uint32_t ring_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&ring[0]));
-  auto stage_lds = [&](int s) { return ring_lds + uint32_t(s) * uint32_t(sizeof(StageTile)); };
+  auto stage_lds = [&](int s) { return ring_lds + uint32_t(s) * uint32_t(sizeof(Stage)); };
   const int qrow = tile * BM + row_in_tile;
   const bool qvalid = qrow < p.n_q;
 
@@ -358,7 +408,7 @@ void attn_jvp_bf16_wide_kernel(KernelParams p) {
   int2 ent_c = n > 0 ? entry(0) : no_ent;
   int2 ent_1 = n > 1 ? entry(1) : no_ent;
   if (n > 0)
-    issue_block<TAN>(stage_lds(0), wave, p, kb_, dkb_, vb_, dvb_, ent_c.x * BN, bits_of(ent_c));
+    issue_block<D, TAN>(stage_lds(0), wave, p, kb_, dkb_, vb_, dvb_, ent_c.x * BN, bits_of(ent_c));
 
   // dQ tile -> LDS (rows past n_q re-read the last row), Q -> registers.
   if (TAN) {
@@ -378,7 +428,7 @@ void attn_jvp_bf16_wide_kernel(KernelParams p) {
                            : static_cast<const void *>(static_cast<const __bf16 *>(dqb) +
                                                        int64_t(rb) * p.q_sn);
       const uint32_t roff = zq ? 0u : uint32_t(grow - rb) * uint32_t(p.q_sn) * 2u;
-      dma16(src, roff + uint32_t(pch ^ k_swz(row)) * 16u,
+      dma16(src, roff + uint32_t(pch ^ k_swz<D>(row)) * 16u,
             dq_base + uint32_t(i * kThreads + wave * 64) * 16u);
     }
   }
@@ -403,14 +453,14 @@ void attn_jvp_bf16_wide_kernel(KernelParams p) {
     wait_vmcnt<0>();  // block j (and, first time, dQ and Q) has landed
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    const StageTile *st = &ring[j & 1];
+    const Stage *st = &ring[j & 1];
     f32x16 S, dS;
-    score_block<TAN>(st, dq_lds, qf, row_in_tile, S, dS);
+    score_block<D, TAN>(st, dq_lds, qf, row_in_tile, S, dS);
     // block j + 1 into the other stage (released by the barrier)
     if (j + 1 < n)
-      issue_block<TAN>(stage_lds((j + 1) & 1), wave, p, kb_, dkb_, vb_, dvb_, ent_1.x * BN,
+      issue_block<D, TAN>(stage_lds((j + 1) & 1), wave, p, kb_, dkb_, vb_, dvb_, ent_1.x * BN,
                        bits_of(ent_1));
-    softmax_value_block<TAN>(st, S, dS, accO, accT, m_ref, l_run, mu_run, ent_c.y >= 0,
+    softmax_value_block<D, TAN>(st, S, dS, accO, accT, m_ref, l_run, mu_run, ent_c.y >= 0,
                              row_in_tile, p.scale_log2, p.scale);
     ent_c = ent_1;
     ent_1 = j + 2 < n ? entry(j + 2) : no_ent;
@@ -472,13 +522,19 @@ void attn_jvp_bf16_wide_kernel(KernelParams p) {
 
 }  // namespace
 
-int launch_bf16_wide(const KernelParams &p, bool tangent, void *stream) {
+int launch_bf16(const KernelParams &p, int D, bool tangent, void *stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int64_t G = int64_t(p.n_tiles) * p.B * p.H;
-  if (tangent)
-    hipLaunchKernelGGL(attn_jvp_bf16_wide_kernel<true>, dim3(unsigned(G)), dim3(kThreads), 0, s, p);
+  const dim3 grid(unsigned(int64_t(p.n_tiles) * p.B * p.H));
+  if (D == 128 && tangent)
+    hipLaunchKernelGGL((attn_jvp_bf16_wide_kernel<128, true>), grid, dim3(kThreads), 0, s, p);
+  else if (D == 128)
+    hipLaunchKernelGGL((attn_jvp_bf16_wide_kernel<128, false>), grid, dim3(kThreads), 0, s, p);
+  else if (D == 64 && tangent)
+    hipLaunchKernelGGL((attn_jvp_bf16_wide_kernel<64, true>), grid, dim3(kThreads), 0, s, p);
+  else if (D == 64)
+    hipLaunchKernelGGL((attn_jvp_bf16_wide_kernel<64, false>), grid, dim3(kThreads), 0, s, p);
   else
-    hipLaunchKernelGGL(attn_jvp_bf16_wide_kernel<false>, dim3(unsigned(G)), dim3(kThreads), 0, s, p);
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

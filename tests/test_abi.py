@@ -36,7 +36,7 @@ def test_version_and_status_strings():
         assert aj.attn_jvp_status_str(st) not in ("", "unknown status")
     assert aj.attn_jvp_status_str(-99) == "unknown status"
     assert aj.attn_jvp_tile_shape(aj.ATTN_JVP_BF16, 128) == (256, 32)
-    assert aj.attn_jvp_tile_shape(aj.ATTN_JVP_BF16, 64) == (128, 32)
+    assert aj.attn_jvp_tile_shape(aj.ATTN_JVP_BF16, 64) == (256, 32)
     assert aj.attn_jvp_tile_shape(aj.ATTN_JVP_F32, 64) == (64, 32)
     with pytest.raises(aj.AttnJvpError):
         aj.attn_jvp_tile_shape(aj.ATTN_JVP_BF16, 96)
@@ -119,15 +119,16 @@ def test_split_rejects_bad_arguments(kw, status):
 
 
 def test_split_workspace_checks():
-    mask = aj.attn_jvp_mask_tf(8, 64, 1)   # n = 1024: 8 tiles of 128 rows at D=64
+    mask = aj.attn_jvp_mask_tf(8, 64, 1)   # n = 1024 rows at D=64
     L = _lib.lib()
     a = _args(mask, D=64, q_stride_n=128, q_stride_h=64, k_stride_n=128, k_stride_h=64)
     need = ctypes.c_uint64(0)
     assert L.attn_jvp_fwd_split_workspace(ctypes.byref(a), mask.handle, 4,
                                           ctypes.byref(need)) == _lib.ATTN_JVP_OK
-    u = aj.attn_jvp_mask_split_schedule(mask, 128, 32, 4)
+    bm, bn = aj.attn_jvp_tile_shape(aj.ATTN_JVP_BF16, 64)
+    u = aj.attn_jvp_mask_split_schedule(mask, bm, bn, 4)
     assert u["n_parts"] > 0
-    rows = 1 * 2 * u["n_parts"] * 128                      # B * H * parts * block_m
+    rows = 1 * 2 * u["n_parts"] * bm                       # B * H * parts * block_m
     assert need.value == rows * 16 + rows * 2 * 64 * 4      # float4 stats + A, T rows
     assert L.attn_jvp_fwd_split_workspace(ctypes.byref(a), mask.handle, 0,
                                           ctypes.byref(need)) == _lib.ATTN_JVP_ERR_SHAPE

@@ -284,31 +284,22 @@ def test_outputs_fully_written_and_in_bounds(dtype):
         assert torch.isfinite(buf[G:-G]).all()
 
 
-# (B, H, n): the B*H slices and n / 128 query tiles select each branch of the
-# workgroup -> work map: XCD groups of 8, 4, 2 and 1 slices' worth, and the
-# identity map when the tiles do not split evenly over a group.
+# (B, H, n): the B*H slices and n / 256 query tiles (both bf16 head dims use
+# 256-row tiles) select each branch of the workgroup -> work map: XCD groups
+# of 8, 4, 2 and 1 slices' worth, and the identity map when the tiles do not
+# split evenly over a group.
 WORK_MAP_CASES = [
-    (1, 3, 1024),  # 3 slices, 8 tiles: one group of 8 XCDs, 1 tile slot in 8 each
-    (1, 2, 512),   # groups of 4 XCDs
-    (2, 3, 256),   # 6 slices: groups of 4 XCDs, 2 tiles -> identity map
-    (1, 4, 300),   # groups of 2 XCDs, 3 tiles -> identity map
-    (2, 5, 512),   # 10 slices: groups of 4 XCDs, 5 slices per group
-    (1, 2, 1024),  # groups of 4 XCDs, 2 tile slots each
-    (4, 2, 200),   # 8 slices: one slice group per XCD
-]
-
-
-# The same branches for head dim 128 (256-row tiles).
-WORK_MAP_CASES_128 = [
-    (1, 3, 2048),  # one group of 8 XCDs
+    (1, 3, 2048),  # 3 slices, 8 tiles: one group of 8 XCDs, 1 tile slot in 8 each
     (1, 2, 1024),  # groups of 4 XCDs
+    (2, 3, 512),   # 6 slices: groups of 4 XCDs, 2 tiles -> identity map
     (1, 4, 600),   # groups of 2 XCDs, 3 tiles -> identity map
+    (2, 5, 1024),  # 10 slices: groups of 4 XCDs, 5 slices per group
+    (1, 2, 2048),  # groups of 4 XCDs, 2 tile slots each
     (4, 2, 400),   # 8 slices: one slice group per XCD
 ]
 
 
-@pytest.mark.parametrize("B,H,n,D", [c + (64,) for c in WORK_MAP_CASES] +
-                         [c + (128,) for c in WORK_MAP_CASES_128])
+@pytest.mark.parametrize("B,H,n,D", [c + (d,) for d in (64, 128) for c in WORK_MAP_CASES])
 def test_every_tile_of_every_slice_computed_once(B, H, n, D):
     say(f"case: dense bf16 B={B} H={H} n={n} D={D} (work map)")
     pred = dense_allowed(n, n)
