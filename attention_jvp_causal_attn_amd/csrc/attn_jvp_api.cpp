@@ -491,7 +491,7 @@ extern "C" int attn_jvp_bwd(const attn_jvp_bwd_args *a, const attn_jvp_mask *m, 
   if (hipGetDevice(&device) != hipSuccess) return ATTN_JVP_ERR_HIP;
   const bool bf16 = a->dtype == ATTN_JVP_BF16;
   const int BM = !bf16 ? attnjvp::kF32BlockM
-                       : (a->D == 128 ? attnjvp::kBwdBlockMWide : attnjvp::kBwdBlockM);
+                       : attnjvp::kBwdBlockMWide;
   const int BN = bf16 ? attnjvp::kBwdBlockN : attnjvp::kF32BlockN;
   const DeviceSchedule *rs = nullptr, *cs = nullptr;
   const attn_jvp_mask *t = nullptr;
@@ -532,8 +532,7 @@ extern "C" int attn_jvp_bwd(const attn_jvp_bwd_args *a, const attn_jvp_mask *m, 
   p.c_bits = cs->partial_bits; p.c_partial = cs->n_partial;
   p.c_map = make_work_map(slices, cs->n_tiles);
   const int err = !bf16 ? attnjvp::launch_bwd_f32(p, a->D, stream)
-                 : a->D == 128 ? attnjvp::launch_bwd_bf16_wide(p, stream)
-                               : attnjvp::launch_bwd_bf16(p, a->D, stream);
+                       : attnjvp::launch_bwd_bf16_wide(p, a->D, stream);
   return err == hipSuccess ? ATTN_JVP_OK : ATTN_JVP_ERR_HIP;
 }
 

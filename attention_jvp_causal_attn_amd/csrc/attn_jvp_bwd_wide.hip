@@ -1,12 +1,35 @@
-// Backward of masked attention for gfx950, head dim 128: the two passes of
-// attn_jvp_bwd.hip (dQ over query tiles, dK/dV over key tiles of the
-// transposed mask; see there for the formulas) with eight waves per
-// workgroup, two per SIMD, over 256 rows (or keys): one wave's softmax-side
-// vector work runs while the other keeps the matrix core busy.  Every value
-// lives in the 256 VGPRs a wave has at two waves per SIMD; the dK/dV pass
-// therefore stages its V rows in LDS (read as the MFMA B operand) while K
-// stays in registers.  Copies go through a 2-stage ring: block j + 1 is
-// copied while block j is computed.
+// Gradients of masked attention (the backward of the primal) for gfx950,
+// bf16 in and out, fp32 accumulate, head dim 64 or 128.
+//
+// The forward returns the row log-sum-exp so that a backward of the same
+// masked operator can reuse it ("Causal-rCM ..." summary, Appendix B: the
+// kernel's outputs are O, LSE and dO; the student is trained through the
+// TF-masked packed forward, Section 3).  With P_ij = exp(s_ij - LSE_i) over
+// the admissible pairs and g = dL/dO:
+//     D_i   = <g_i, O_i>
+//     dP_ij = <g_i, v_j>,   dS_ij = P_ij (dP_ij - D_i)
+//     dQ_i  = scale sum_j dS_ij k_j,   dK_j = scale sum_i dS_ij q_i,
+//     dV_j  = sum_i P_ij g_i.
+// Two passes, no atomics (deterministic):
+//  * dQ pass: a workgroup owns 256 query rows and walks the mask's schedule
+//    of admissible 32-key blocks: S^T = K Q^T and dP^T = V g^T (Q and g in
+//    registers as MFMA B operands, K and V from LDS), dS^T, then
+//    dQ^T += K^T dS^T with K^T read transposed from the same LDS tile.  It
+//    also computes D_i (from O and g) and stores it for the second pass;
+//  * dK/dV pass: a workgroup owns 256 keys and walks the schedule of the
+//    transposed mask (admissible 32-query blocks): S = Q K^T, dP = g V^T (K
+//    in registers, V and the Q and g blocks from LDS), then dV^T += g^T P
+//    and dK^T += Q^T dS.
+// Eight waves per workgroup, two per SIMD, 32 rows (or keys) each: one
+// wave's softmax-side vector work runs while the other keeps the matrix core
+// busy.  Every value lives in the 256 VGPRs a wave has at two waves per
+// SIMD; the dK/dV pass therefore stages its V rows in LDS (read as the MFMA
+// B operand) while K stays in registers.  Both passes use one lane per row
+// in each half-wave, the row permutation that puts a lane's 8 weights of a
+// 16-wide step in register order, direct-to-LDS copies into a 2-stage ring
+// (block j + 1 is copied while block j is computed), and tiles swizzled so
+// that both row reads (ds_read_b128) and transposed reads
+// (ds_read_b64_tr_b16) hit distinct banks.
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
@@ -23,15 +46,21 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int D = 128;
 constexpr int kThreads = 512;
 constexpr int BM = kBwdBlockMWide;  // 256 rows (or keys) per workgroup
 constexpr int BN = kBwdBlockN;      // 32 keys (or queries) per block
-constexpr int KCH = D / 8;
-constexpr int KSTEPS = D / 16;
-constexpr int DT = D / 32;
 constexpr int kEntChunk = 512;
-static_assert(BM == 256 && BN == 32 && BN * KCH == kThreads, "one chunk per lane per tile");
+static_assert(BM == 256 && BN == 32, "8 waves x 32 rows, 32-row blocks");
+
+// Per head dim: 16-byte chunks per row, 16-wide k-steps, 32-wide dim tiles.
+template <int D>
+struct Geo {
+  static_assert(D == 64 || D == 128, "head dim 64 or 128");
+  static constexpr int KCH = D / 8;
+  static constexpr int KSTEPS = D / 16;
+  static constexpr int DT = D / 32;
+  static constexpr int TILE = BN * KCH;  // chunks of one 32-row tile
+};
 constexpr float kLog2e = 1.44269504088896340736f;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 x) { return __builtin_bit_cast(bf16x8, x); }
@@ -44,13 +73,24 @@ __device__ __forceinline__ bf16x8 to_bf16x8(const float *x) {
   return __builtin_convertvector(v, bf16x8);
 }
 __device__ __forceinline__ float xor32(float v) { return __shfl_xor(v, 32, 64); }
-// Bits 2 and 3 of a 32-row tile index swapped (see attn_jvp_bwd.hip).
+// Bits 2 and 3 of a 32-row tile index swapped: the MFMA output element
+// (row 8j + 4h + i) of a tile whose A-operand rows are read in this order
+// holds row 16(j/2) + 8h + 4(j%2) + i, so lane-half h owns rows 16s + 8h + 0..7
+// of step s in register order.
 __device__ __forceinline__ int swap_bits23(int m) {
   return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
 }
-// Chunk swizzle of 256-byte rows, conflict-free for row and transposed reads
-// (see attn_jvp_bwd.hip).
-__device__ __forceinline__ int sw(int row) { return 2 * (row & 7) | ((row >> 3) & 1); }
+// 16-byte-chunk XOR swizzle of a row, conflict-free both for row reads (16
+// lanes read 16 rows at one chunk) and for transposed reads (16 lanes read 4
+// consecutive rows x 32 bytes).  Head dim 128 (256-byte rows): a bijection of
+// the row's low 4 bits whose high 3 bits (the 32-byte window) differ across 4
+// consecutive rows.  Head dim 64 (128-byte rows, two rows per 256-byte bank
+// cycle): a bijection within each row parity whose window bits differ between
+// rows 4a and 4a+2 (and 4a+1, 4a+3).
+template <int D>
+__device__ __forceinline__ int sw(int row) {
+  return D == 128 ? (2 * (row & 7) | ((row >> 3) & 1)) : (2 * ((row >> 1) & 3) | ((row >> 3) & 1));
+}
 
 // 16 bytes per lane straight into LDS at lds_wave + 16 * lane (lds_wave
 // wave-uniform); tracked by vmcnt and waited for explicitly.  One wait state
@@ -76,47 +116,66 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// This lane's copy chunk of a 32-row block (swizzled); rows past the last
+// Byte offset of chunk q of a 32-row block (swizzled); rows past the last
 // valid one re-read it (masked out by the schedule).
-__device__ __forceinline__ uint32_t copy_offset(int64_t row_stride, int rows_valid) {
-  const int q = int(threadIdx.x);
+template <int D>
+__device__ __forceinline__ uint32_t copy_offset(int q, int64_t row_stride, int rows_valid) {
+  constexpr int KCH = Geo<D>::KCH;
   const int row = q / KCH, pch = q % KCH;
   return uint32_t(min(row, rows_valid - 1)) * uint32_t(row_stride) * 2u +
-         uint32_t(pch ^ sw(row)) * 16u;
+         uint32_t(pch ^ sw<D>(row)) * 16u;
 }
 
-// Two 32 x 128 tiles (rows r0 .. r0+31 of a and b) and the block's 256 mask
-// words into a stage.
+// Two 32 x D tiles (rows r0 .. r0+31 of a and b) and the block's 256 mask
+// words into a stage.  Head dim 128: one chunk per lane per tile; head dim
+// 64: waves 0-3 copy a, waves 4-7 copy b.
+template <int D>
 __device__ __forceinline__ void copy_pair(uint32_t st, uint32_t a_at, uint32_t b_at,
                                           uint32_t bits_at, int wave, const __bf16 *a,
                                           const __bf16 *b, int64_t row_stride, int r0, int n_rows,
                                           const uint32_t *bits_src) {
   const int lane = threadIdx.x & 63;
   const int64_t boff = int64_t(r0) * row_stride;
-  const uint32_t off = copy_offset(row_stride, min(BN, n_rows - r0));
-  const uint32_t chunk = uint32_t(wave * 64) * 16u;
-  dma16(a + boff, off, st + a_at + chunk);
-  dma16(b + boff, off, st + b_at + chunk);
+  if constexpr (D == 128) {
+    const uint32_t off = copy_offset<D>(int(threadIdx.x), row_stride, min(BN, n_rows - r0));
+    const uint32_t chunk = uint32_t(wave * 64) * 16u;
+    dma16(a + boff, off, st + a_at + chunk);
+    dma16(b + boff, off, st + b_at + chunk);
+  } else {
+    const int c0 = (wave & 3) * 64;  // this wave's chunks of its tile
+    const uint32_t off = copy_offset<D>(c0 + lane, row_stride, min(BN, n_rows - r0));
+    dma16((wave < 4 ? a : b) + boff, off, st + (wave < 4 ? a_at : b_at) + uint32_t(c0) * 16u);
+  }
   // mask bits: BM words = 64 chunks; wave w copies chunks 8w .. 8w+7 (lanes 0..7)
   if (lane < 8)
     dma16(bits_src, uint32_t(wave * 8 + lane) * 16u, st + bits_at + uint32_t(wave) * 128u);
 }
 
+// A-operand row read of a swizzled 32 x D tile: this lane's row (permuted)
+// at k-step t.
+template <int D>
 __device__ __forceinline__ bf16x8 row_operand(const uint4 *tile, int prow, int t, int hh) {
-  return as_bf16x8(tile[prow * KCH + ((2 * t + hh) ^ sw(prow))]);
+  return as_bf16x8(tile[prow * Geo<D>::KCH + ((2 * t + hh) ^ sw<D>(prow))]);
 }
+// A-operand transposed read of a swizzled 32 x D tile for step s of 16
+// rows and dim tile nt: within each 16-lane group, lane jl reads row
+// (16s + 4*half + krel) at dims (d0 + 4*(jl%4)) .. +3.
+template <int D>
 __device__ __forceinline__ bf16x8 tr_operand(const uint4 *tile, int s, int nt, int dcol, int krel) {
   bf16x4 h[2];
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     const int row = 16 * s + 4 * half + krel;
     const int d = 32 * nt + dcol;
-    const int chunk = row * KCH + ((d >> 3) ^ sw(row));
+    const int chunk = row * Geo<D>::KCH + ((d >> 3) ^ sw<D>(row));
     const char *ptr = reinterpret_cast<const char *>(tile + chunk) + (d & 7) * 2;
     h[half] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4 *)(ptr));
   }
   return __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7);
 }
+// Register-order position of element r of a 16-wide half-tile: row (or
+// column) 16(j/2) + 8h + 4(j%2) + i for r = 4j + i; shifted by 8h, the bit of a
+// 32-bit mask word.
 __device__ __forceinline__ int reg_pos(int r) {
   const int j = r >> 2, i = r & 3;
   return 16 * (j >> 1) + 4 * (j & 1) + i;
@@ -138,14 +197,18 @@ __device__ __forceinline__ TrLane tr_lane() {
 
 // ---------------------------------------------------------------- dQ pass
 
+template <int D>
 struct alignas(16) KVTile {
-  uint4 k[BN * KCH];
-  uint4 v[BN * KCH];
+  uint4 k[Geo<D>::TILE];
+  uint4 v[Geo<D>::TILE];
   uint32_t bits[BM];
 };
 
+template <int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_wide_kernel(BwdParams p) {
+  constexpr int KSTEPS = Geo<D>::KSTEPS, DT = Geo<D>::DT;
+  using KVTile = attnjvp::KVTile<D>;
   __shared__ KVTile ring[2];
   __shared__ int2 ents[2][kEntChunk];
   const int L = work_item(int(blockIdx.x), p.r_map);
@@ -183,7 +246,7 @@ void bwd_dq_wide_kernel(BwdParams p) {
   };
   auto bits_of = [&](int2 e) { return p.r_bits + int64_t(e.y >= 0 ? e.y : p.r_partial) * BM; };
   auto issue = [&](int s, int2 e) {
-    copy_pair(stage_lds(s), offsetof(KVTile, k), offsetof(KVTile, v), offsetof(KVTile, bits), wave,
+    copy_pair<D>(stage_lds(s), offsetof(KVTile, k), offsetof(KVTile, v), offsetof(KVTile, bits), wave,
               kb, vb, p.k_sn, e.x * BN, p.n_k, bits_of(e));
   };
 
@@ -229,8 +292,8 @@ void bwd_dq_wide_kernel(BwdParams p) {
     f32x16 S = {}, G = {};
 #pragma unroll
     for (int t = 0; t < KSTEPS; ++t) {
-      S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand(st->k, krow, t, hh), qf[t], S, 0, 0, 0);
-      G = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand(st->v, krow, t, hh), gf[t], G, 0, 0, 0);
+      S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(st->k, krow, t, hh), qf[t], S, 0, 0, 0);
+      G = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(st->v, krow, t, hh), gf[t], G, 0, 0, 0);
       if (t % 4 == 3) __builtin_amdgcn_sched_barrier(0);  // bound the operand prefetch
     }
     if (j + 1 < n) issue((j + 1) & 1, entry(j + 1));  // its stage was released by the barrier
@@ -250,7 +313,7 @@ void bwd_dq_wide_kernel(BwdParams p) {
     for (int s = 0; s < 2; ++s) {
 #pragma unroll
       for (int nt = 0; nt < DT; ++nt) {
-        acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(st->k, s, nt, tl.dcol, tl.krel),
+        acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(st->k, s, nt, tl.dcol, tl.krel),
                                                           gsb[s], acc[nt], 0, 0, 0);
         if (nt % 4 == 3) __builtin_amdgcn_sched_barrier(0);
       }
@@ -275,17 +338,21 @@ void bwd_dq_wide_kernel(BwdParams p) {
 
 // ------------------------------------------------------------ dK/dV pass
 
+template <int D>
 struct alignas(16) QGTile {
-  uint4 q[BN * KCH];
-  uint4 g[BN * KCH];
+  uint4 q[Geo<D>::TILE];
+  uint4 g[Geo<D>::TILE];
   float ld[8 * 8];  // wave w's region: LSE of queries 4w .. 4w+3, then their D
   uint32_t bits[BM];
 };
 
+template <int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkv_wide_kernel(BwdParams p) {
+  constexpr int KCH = Geo<D>::KCH, KSTEPS = Geo<D>::KSTEPS, DT = Geo<D>::DT;
+  using QGTile = attnjvp::QGTile<D>;
   __shared__ QGTile ring[2];
-  __shared__ uint4 v_lds[BM * KCH];  // this tile's V rows (B operands), 64 KB
+  __shared__ uint4 v_lds[BM * KCH];  // this tile's V rows (B operands), 64 KB at D = 128
   __shared__ int2 ents[2][kEntChunk];
   const int L = work_item(int(blockIdx.x), p.c_map);
   const int slot = L % p.c_map.n_tiles;
@@ -323,7 +390,7 @@ void bwd_dkv_wide_kernel(BwdParams p) {
   auto bits_of = [&](int2 e) { return p.c_bits + int64_t(e.y >= 0 ? e.y : p.c_partial) * BM; };
   auto issue = [&](int s, int2 e) {
     const int q0 = e.x * BN;
-    copy_pair(stage_lds(s), offsetof(QGTile, q), offsetof(QGTile, g), offsetof(QGTile, bits), wave,
+    copy_pair<D>(stage_lds(s), offsetof(QGTile, q), offsetof(QGTile, g), offsetof(QGTile, bits), wave,
               qb, gb, p.q_sn, q0, p.n_q, bits_of(e));
     // LSE and D of queries q0 + 4w .. q0 + 4w + 3 (lanes 0..3, 4..7), clamped
     if (lane < 8) {
@@ -342,14 +409,14 @@ void bwd_dkv_wide_kernel(BwdParams p) {
     const __bf16 *vb = static_cast<const __bf16 *>(p.v) + koff;
 #pragma unroll
     for (int i = 0; i < BM * KCH / kThreads; ++i) {
-      // 32 rows per step: a 64-bit base at the step's first (clamped) row,
-      // 32-bit lane offsets inside it
+      // kThreads / KCH rows per step: a 64-bit base at the step's first
+      // (clamped) row, 32-bit lane offsets inside it
       const int q = i * kThreads + threadIdx.x;
       const int row = q / KCH, pch = q % KCH;
       const int rb = min(tile * BM + i * (kThreads / KCH), p.n_k - 1);
       const int grow = min(tile * BM + row, p.n_k - 1);
       dma16(vb + int64_t(rb) * p.k_sn,
-            uint32_t(grow - rb) * uint32_t(p.k_sn) * 2u + uint32_t(pch ^ sw(row)) * 16u,
+            uint32_t(grow - rb) * uint32_t(p.k_sn) * 2u + uint32_t(pch ^ sw<D>(row)) * 16u,
             v_base + uint32_t(i * kThreads + wave * 64) * 16u);
     }
   }
@@ -382,9 +449,9 @@ void bwd_dkv_wide_kernel(BwdParams p) {
     f32x16 S = {}, G = {};
 #pragma unroll
     for (int t = 0; t < KSTEPS; ++t) {
-      const bf16x8 vf = as_bf16x8(vrow[(2 * t + hh) ^ sw(key_in_tile)]);
-      S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand(st->q, qperm, t, hh), kf[t], S, 0, 0, 0);
-      G = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand(st->g, qperm, t, hh), vf, G, 0, 0, 0);
+      const bf16x8 vf = as_bf16x8(vrow[(2 * t + hh) ^ sw<D>(key_in_tile)]);
+      S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(st->q, qperm, t, hh), kf[t], S, 0, 0, 0);
+      G = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(st->g, qperm, t, hh), vf, G, 0, 0, 0);
       if (t % 4 == 3) __builtin_amdgcn_sched_barrier(0);  // bound the operand prefetch
     }
     if (j + 1 < n) issue((j + 1) & 1, entry(j + 1));  // its stage was released by the barrier
@@ -423,9 +490,9 @@ void bwd_dkv_wide_kernel(BwdParams p) {
     for (int s = 0; s < 2; ++s) {
 #pragma unroll
       for (int nt = 0; nt < DT; ++nt) {
-        accV[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(st->g, s, nt, tl.dcol, tl.krel),
+        accV[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(st->g, s, nt, tl.dcol, tl.krel),
                                                            pb[s], accV[nt], 0, 0, 0);
-        accK[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(st->q, s, nt, tl.dcol, tl.krel),
+        accK[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(st->q, s, nt, tl.dcol, tl.krel),
                                                            gsb[s], accK[nt], 0, 0, 0);
         if (nt % 4 == 3) __builtin_amdgcn_sched_barrier(0);
       }
@@ -454,18 +521,25 @@ void bwd_dkv_wide_kernel(BwdParams p) {
   }
 }
 
-}  // namespace
-
-int launch_bwd_bf16_wide(const BwdParams &p, void *stream) {
-  hipStream_t s = static_cast<hipStream_t>(stream);
+template <int D>
+hipError_t launch(const BwdParams &p, hipStream_t s) {
   const int64_t Gq = int64_t(p.r_map.n_tiles) * p.B * p.H;
   const int64_t Gk = int64_t(p.c_map.n_tiles) * p.B * p.H;
   // the dQ pass stores D, which the dK/dV pass reads: same stream, in order
-  hipLaunchKernelGGL(bwd_dq_wide_kernel, dim3(unsigned(Gq)), dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL((bwd_dq_wide_kernel<D>), dim3(unsigned(Gq)), dim3(kThreads), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_dkv_wide_kernel, dim3(unsigned(Gk)), dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL((bwd_dkv_wide_kernel<D>), dim3(unsigned(Gk)), dim3(kThreads), 0, s, p);
   return hipGetLastError();
+}
+
+}  // namespace
+
+int launch_bwd_bf16_wide(const BwdParams &p, int D, void *stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (D == 128) return launch<128>(p, s);
+  if (D == 64) return launch<64>(p, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace attnjvp

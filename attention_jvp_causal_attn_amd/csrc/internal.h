@@ -219,8 +219,7 @@ const HostSplit *host_split_locked(const attn_jvp_mask *m, int block_m, int bloc
 
 // Kernel launchers (defined in the .hip files).  Return a hipError_t value.
 int launch_bf16(const KernelParams &p, int D, bool tangent, void *stream);
-int launch_bwd_bf16(const BwdParams &p, int D, void *stream);
-int launch_bwd_bf16_wide(const BwdParams &p, void *stream);  // D = 128
+int launch_bwd_bf16_wide(const BwdParams &p, int D, void *stream);
 int launch_bwd_f32(const BwdParams &p, int D, void *stream);
 int launch_f32(const KernelParams &p, int D, bool tangent, void *stream);
 int launch_merge(const MergeParams &p, int D, bool bf16, bool tangent, void *stream);
@@ -228,8 +227,7 @@ int launch_merge(const MergeParams &p, int D, bool bf16, bool tangent, void *str
 // Tile shapes of the kernels.
 constexpr int kBf16BlockMWide = 256;  // 8 waves x 32 rows (head dims 64 and 128)
 constexpr int kBf16BlockN = 32;
-constexpr int kBwdBlockM = 128;       // backward, head dim 64: 4 waves x 32 rows (or keys)
-constexpr int kBwdBlockMWide = 256;   // backward, head dim 128: 8 waves x 32 rows (or keys)
+constexpr int kBwdBlockMWide = 256;   // backward: 8 waves x 32 rows (or keys)
 constexpr int kBwdBlockN = 32;        // backward: blocks of 32 keys (or queries)
 constexpr int kF32BlockM = 64;
 constexpr int kF32BlockN = 32;

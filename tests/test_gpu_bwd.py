@@ -64,6 +64,7 @@ SMALL = [
     (3, 100, 3, 2, 1),  # one chunk of 300 tokens per stream
     (2, 1, 1, 1, 1),    # N=4: rows with a single admissible key
     (9, 33, 3, 1, 1),
+    (8, 130, 2, 1, 2),  # N=1040: five 256-row tiles, ragged tail
 ]
 
 
@@ -77,7 +78,8 @@ def test_small_tf_bwd(nf, tpf, fpc, B, H, D):
     parity(x, g, pred, aj.attn_jvp_mask_tf(nf, tpf, fpc))
 
 
-def test_rect_bwd_queries_differ_from_keys():
+@pytest.mark.parametrize("D", [128, 64])
+def test_rect_bwd_queries_differ_from_keys(D):
     # queries of the current chunk against a longer key sequence, with keys
     # that no query sees (their gradients are zero)
     n_q, n_k = 150, 420
@@ -88,8 +90,8 @@ def test_rect_bwd_queries_differ_from_keys():
     ke = [300, 140, 330]
     pred = rects_allowed(n_q, n_k, rects)
     mask = aj.attn_jvp_mask_rects(n_q, n_k, gq, rp, kb, ke)
-    xq = make_random(1, n_q, 2, 128, dtype="bf16", seed=9700)
-    xk = make_random(1, n_k, 2, 128, dtype="bf16", seed=9710)
+    xq = make_random(1, n_q, 2, D, dtype="bf16", seed=9700)
+    xk = make_random(1, n_k, 2, D, dtype="bf16", seed=9710)
     x = {"q": xq["q"], "k": xk["k"], "v": xk["v"]}
     g = xq["dq"]
     gq_, gk_, gv_, _ = run_bwd(x, g, mask)
@@ -97,10 +99,11 @@ def test_rect_bwd_queries_differ_from_keys():
     parity(x, g, pred, mask)
 
 
-def test_dense_bwd():
+@pytest.mark.parametrize("D", [128, 64])
+def test_dense_bwd(D):
     pred = dense_allowed(300, 300)
-    x = make_random(2, 300, 2, 128, dtype="bf16", seed=9800)
-    g = make_random(2, 300, 2, 128, dtype="bf16", seed=9810)["q"]
+    x = make_random(2, 300, 2, D, dtype="bf16", seed=9800)
+    g = make_random(2, 300, 2, D, dtype="bf16", seed=9810)["q"]
     parity(x, g, pred, aj.attn_jvp_mask_dense(300, 300))
 
 
