@@ -99,17 +99,21 @@ struct alignas(16) StageTile {
 __device__ __forceinline__ int swap_bits23(int m) {
   return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
 }
-// 16-byte-chunk XOR swizzles: row-operand reads (K, dK, dQ) touch 16 rows at
-// one chunk; transposed reads (V, dV) touch 4 rows x 4 chunks.  Head dim 128
-// (256-byte rows): one swizzle for each access; head dim 64 (128-byte rows):
-// one swizzle conflict-free for both.
+// 16-byte-chunk XOR swizzles, with 64 banks of 4 bytes: row-operand reads
+// (K, dK, dQ; ds_read_b128, 16 lanes per cycle) touch 16 aligned rows at one
+// chunk; transposed reads (V, dV; ds_read_b64_tr_b16, 32 lanes per cycle)
+// touch 4 aligned consecutive rows x 4 consecutive chunks.  Head dim 128
+// (256-byte rows): one swizzle for each access; head dim 64 (128-byte rows,
+// two per bank cycle): one swizzle conflict-free for both (a bijection of 0..7
+// within each row parity over 16 rows whose top bit differs between rows 4a
+// and 4a+2).
 template <int D>
 __device__ __forceinline__ int k_swz(int row) {
-  return D == 128 ? (row & 15) : (2 * ((row >> 1) & 3) | ((row >> 3) & 1));
+  return D == 128 ? (row & 15) : (4 * ((row >> 1) & 1) | ((row >> 2) & 3));
 }
 template <int D>
 __device__ __forceinline__ int v_swz(int row) {
-  return D == 128 ? 4 * (row & 3) : (2 * ((row >> 1) & 3) | ((row >> 3) & 1));
+  return D == 128 ? 4 * (row & 3) : (4 * ((row >> 1) & 1) | ((row >> 2) & 3));
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 x) { return __builtin_bit_cast(bf16x8, x); }

@@ -80,16 +80,18 @@ __device__ __forceinline__ float xor32(float v) { return __shfl_xor(v, 32, 64); 
 __device__ __forceinline__ int swap_bits23(int m) {
   return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
 }
-// 16-byte-chunk XOR swizzle of a row, conflict-free both for row reads (16
-// lanes read 16 rows at one chunk) and for transposed reads (16 lanes read 4
-// consecutive rows x 32 bytes).  Head dim 128 (256-byte rows): a bijection of
-// the row's low 4 bits whose high 3 bits (the 32-byte window) differ across 4
-// consecutive rows.  Head dim 64 (128-byte rows, two rows per 256-byte bank
-// cycle): a bijection within each row parity whose window bits differ between
-// rows 4a and 4a+2 (and 4a+1, 4a+3).
+// 16-byte-chunk XOR swizzle of a row, conflict-free both for row reads
+// (ds_read_b128: 16 lanes per cycle read 16 aligned rows at one chunk) and for
+// transposed reads (ds_read_b64_tr_b16: 32 lanes per cycle read 4 aligned
+// consecutive rows x 4 consecutive chunks), with 64 banks of 4 bytes.  Head
+// dim 128 (256-byte rows, 16 chunk slots per bank cycle): a bijection of the
+// row's low 4 bits whose top two bits (the 64-byte window) differ across 4
+// consecutive rows.  Head dim 64 (128-byte rows, two rows per bank cycle): a
+// bijection of 0..7 within each row parity over 16 rows whose top bit differs
+// between rows 4a and 4a+2 (and 4a+1, 4a+3).
 template <int D>
 __device__ __forceinline__ int sw(int row) {
-  return D == 128 ? (2 * (row & 7) | ((row >> 3) & 1)) : (2 * ((row >> 1) & 3) | ((row >> 3) & 1));
+  return D == 128 ? (4 * (row & 3) | ((row >> 2) & 3)) : (4 * ((row >> 1) & 1) | ((row >> 2) & 3));
 }
 
 // 16 bytes per lane straight into LDS at lds_wave + 16 * lane (lds_wave
@@ -186,6 +188,11 @@ __device__ __forceinline__ int reg_pos(int r) {
 struct TrLane {
   int dcol, krel;
 };
+__device__ __forceinline__ TrLane tr_lane_plain() {
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4, jl = lane & 15;
+  return {16 * (g & 1) + 4 * (jl & 3), 8 * (lane >> 5) + (jl >> 2)};
+}
 __device__ __forceinline__ TrLane tr_lane() {
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4, jl = lane & 15;
@@ -280,15 +287,18 @@ void bwd_dq_wide_kernel(BwdParams p) {
   for (int nt = 0; nt < DT; ++nt) acc[nt] = f32x16{};
   const float sl2 = p.scale_log2;
 
-  for (int j = 0; j < n; ++j) {
+  // Per-lane LDS read offsets, held across the key loop (registers allow it
+  // in this pass); the loop below is unrolled by two so that the ring stage
+  // of every read is an immediate offset.
+  const int krow = swap_bits23(col);
+  const TrLane tl = tr_lane_plain();
+  // One block: S^T, dP^T, dS^T and the dQ update.
+  auto step = [&](int j, const KVTile *st, int next_stage) __attribute__((always_inline)) {
     if ((j + 1) % kEntChunk == 0 && j + 1 < n) load_entries((j + 1) / kEntChunk);
     wait_vmcnt<0>();  // block j (and, first time, Q, g, O) has landed
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    const KVTile *st = &ring[j & 1];
     const int2 ent = entry(j);
-    int krow = swap_bits23(col);
-    asm volatile("" : "+v"(krow));
     f32x16 S = {}, G = {};
 #pragma unroll
     for (int t = 0; t < KSTEPS; ++t) {
@@ -296,19 +306,23 @@ void bwd_dq_wide_kernel(BwdParams p) {
       G = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(st->v, krow, t, hh), gf[t], G, 0, 0, 0);
       if (t % 4 == 3) __builtin_amdgcn_sched_barrier(0);  // bound the operand prefetch
     }
-    if (j + 1 < n) issue((j + 1) & 1, entry(j + 1));  // its stage was released by the barrier
-    const uint32_t bits = ent.y >= 0 ? st->bits[row_in_tile] >> (8 * hh) : ~0u;
-    float gs[16];
+    if (j + 1 < n) issue(next_stage, entry(j + 1));  // its stage was released by the barrier
+    // exponents; in a partial block those of inadmissible pairs become -inf
+    // (exp2 then gives exactly 0, also for a row without keys, whose LSE is
+    // -inf); full blocks skip the mask
+    float x[16], gs[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const bool ok = (bits >> reg_pos(r)) & 1u;
-      const float pr = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], sl2, -lse2)) : 0.f;
-      gs[r] = pr * (G[r] - dsum);
+    for (int r = 0; r < 16; ++r) x[r] = __builtin_fmaf(S[r], sl2, -lse2);
+    if (ent.y >= 0) {
+      const uint32_t bits = st->bits[row_in_tile] >> (8 * hh);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x[r] = (bits >> reg_pos(r)) & 1u ? x[r] : -__builtin_inff();
     }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) gs[r] = __builtin_amdgcn_exp2f(x[r]) * (G[r] - dsum);
     bf16x8 gsb[2];
     gsb[0] = to_bf16x8(gs);
     gsb[1] = to_bf16x8(gs + 8);
-    const TrLane tl = tr_lane();
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
 #pragma unroll
@@ -318,6 +332,10 @@ void bwd_dq_wide_kernel(BwdParams p) {
         if (nt % 4 == 3) __builtin_amdgcn_sched_barrier(0);
       }
     }
+  };
+  for (int j = 0; j < n; j += 2) {
+    step(j, &ring[0], 1);
+    if (j + 1 < n) step(j + 1, &ring[1], 0);
   }
   wait_vmcnt<0>();
 
@@ -436,15 +454,24 @@ void bwd_dkv_wide_kernel(BwdParams p) {
   }
   const float sl2 = p.scale_log2;
 
-  for (int j = 0; j < n; ++j) {
+  // Per-lane LDS read offsets: held across the key loop at head dim 64;
+  // rebuilt per block at head dim 128, where the registers are all taken.
+  // The loop is unrolled by two as in the dQ pass.
+  constexpr bool kHoist = D == 64;
+  const int qperm_h = swap_bits23(col);
+  const TrLane tl_h = tr_lane_plain();
+  // One block of 32 queries: S, dP, dS and the dK, dV updates.
+  auto step = [&](int j, const QGTile *st, int next_stage) __attribute__((always_inline)) {
     if ((j + 1) % kEntChunk == 0 && j + 1 < n) load_entries((j + 1) / kEntChunk);
     wait_vmcnt<0>();  // block j (and, first time, V and K) has landed
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    const QGTile *st = &ring[j & 1];
     const int2 ent = entry(j);
-    int qperm = swap_bits23(col);
-    asm volatile("" : "+v"(qperm));
+    int qperm = qperm_h;
+    if (!kHoist) {
+      qperm = swap_bits23(col);
+      asm volatile("" : "+v"(qperm));
+    }
     const uint4 *vrow = v_lds + key_in_tile * KCH;
     f32x16 S = {}, G = {};
 #pragma unroll
@@ -454,7 +481,7 @@ void bwd_dkv_wide_kernel(BwdParams p) {
       G = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(st->g, qperm, t, hh), vf, G, 0, 0, 0);
       if (t % 4 == 3) __builtin_amdgcn_sched_barrier(0);  // bound the operand prefetch
     }
-    if (j + 1 < n) issue((j + 1) & 1, entry(j + 1));  // its stage was released by the barrier
+    if (j + 1 < n) issue(next_stage, entry(j + 1));  // its stage was released by the barrier
     // LSE and D of this lane's 16 queries 8hh + {0..7} and 16 + 8hh + {0..7}:
     // query q sits in region q / 4 at slot q % 4 (LSE) and 4 + q % 4 (D)
     float lq[16], dq[16];
@@ -470,14 +497,23 @@ void bwd_dkv_wide_kernel(BwdParams p) {
         dq[8 * half + 4 * rg + 2] = b.z; dq[8 * half + 4 * rg + 3] = b.w;
       }
     }
-    const uint32_t bits = ent.y >= 0 ? st->bits[key_in_tile] >> (8 * hh) : ~0u;
+    // partial block: scores of inadmissible pairs to -inf (scale > 0), whose
+    // probability exp2 then makes exactly 0, and the LSE of a query without
+    // keys (-inf) to 0 so that its pairs, all inadmissible, stay at exp2(-inf);
+    // full blocks skip the mask
+    if (ent.y >= 0) {
+      const uint32_t bits = st->bits[key_in_tile] >> (8 * hh);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) S[r] = (bits >> reg_pos(r)) & 1u ? S[r] : -__builtin_inff();
+#pragma unroll
+      for (int e = 0; e < 16; ++e) lq[e] = lq[e] == -__builtin_inff() ? 0.f : lq[e];
+    }
     float pr[16], gs[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int pos = reg_pos(r);
       const int e = 8 * (pos >> 4) + (pos & 7);
-      const bool ok = (bits >> pos) & 1u;
-      pr[r] = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], sl2, -lq[e] * kLog2e)) : 0.f;
+      pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], sl2, -lq[e] * kLog2e));
       gs[r] = pr[r] * (G[r] - dq[e]);
     }
     bf16x8 pb[2], gsb[2];
@@ -485,7 +521,7 @@ void bwd_dkv_wide_kernel(BwdParams p) {
     pb[1] = to_bf16x8(pr + 8);
     gsb[0] = to_bf16x8(gs);
     gsb[1] = to_bf16x8(gs + 8);
-    const TrLane tl = tr_lane();
+    const TrLane tl = kHoist ? tl_h : tr_lane();
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
 #pragma unroll
@@ -497,6 +533,10 @@ void bwd_dkv_wide_kernel(BwdParams p) {
         if (nt % 4 == 3) __builtin_amdgcn_sched_barrier(0);
       }
     }
+  };
+  for (int j = 0; j < n; j += 2) {
+    step(j, &ring[0], 1);
+    if (j + 1 < n) step(j + 1, &ring[1], 0);
   }
   wait_vmcnt<0>();
 

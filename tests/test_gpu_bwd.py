@@ -185,3 +185,21 @@ def test_rect_bwd_fp32_unseen_keys_and_empty_rows():
     check("dQ", f64(gq), dQ, 1e-5)
     check("dK", f64(gk), dK, 1e-5)
     check("dV", f64(gv), dV, 1e-5)
+
+
+@pytest.mark.parametrize("D", [128, 64])
+def test_rect_bwd_bf16_unseen_keys_and_empty_rows(D):
+    # rows 250..329 see nothing (LSE = -inf), keys 520..699 are seen by nobody;
+    # partial blocks then hold rows and queries without any admissible key
+    n_q, n_k, H = 600, 700, 2
+    gq_, rp, kb, ke = [0, 250, 330, 600], [0, 1, 1, 3], [0, 37, 500], [400, 460, 520]
+    pred = rects_allowed(n_q, n_k, [(0, 250, 0, 400), (330, 600, 37, 460), (330, 600, 500, 520)])
+    xq = make_random(1, n_q, H, D, dtype="bf16", seed=9920 + D)
+    xk = make_random(1, n_k, H, D, dtype="bf16", seed=9921 + D)
+    x = dict(q=xq["q"], k=xk["k"], v=xk["v"])
+    g = make_random(1, n_q, H, D, dtype="bf16", seed=9922 + D)["q"]
+    mask = aj.attn_jvp_mask_rects(n_q, n_k, gq_, rp, kb, ke)
+    gq, gk, gv, delta = run_bwd(x, g, mask)
+    assert torch.all(gq[:, 250:330] == 0) and torch.all(gk[:, 520:] == 0) and torch.all(gv[:, 520:] == 0)
+    assert torch.all(delta[:, :, 250:330] == 0)
+    parity(x, g, pred, mask)
