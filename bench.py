@@ -79,6 +79,61 @@ def time_calls(fn, steps, warmup, stream):
     return total / steps, per
 
 
+def clock_under_load(fn, n_calls=60):
+    """The GPU's current shader and memory clocks, as the driver reports them
+    in sysfs (pp_dpm_sclk / pp_dpm_mclk, the line marked '*'), sampled every
+    20 ms while untimed calls of ``fn`` keep the GPU busy (about a second of
+    queued work): min / median / max in MHz.  None when the files are not
+    readable."""
+    import threading
+    import torch
+    try:
+        pr = torch.cuda.get_device_properties(0)
+        dev = "/sys/bus/pci/devices/%04x:%02x:%02x.0" % (pr.pci_domain_id, pr.pci_bus_id,
+                                                         pr.pci_device_id)
+    except Exception:  # noqa: BLE001 - no PCI address, no record
+        return None
+    files = {k: os.path.join(dev, "pp_dpm_" + k) for k in ("sclk", "mclk")}
+    if not all(os.access(f, os.R_OK) for f in files.values()):
+        return None
+
+    def current(path):
+        with open(path) as f:
+            for line in f:
+                if line.rstrip().endswith("*"):
+                    m = re.search(r"(\d+)\s*mhz", line.lower())
+                    return int(m.group(1)) if m else None
+        return None
+
+    samples = {k: [] for k in files}
+    done = threading.Event()
+
+    def sample():
+        while not done.is_set():
+            for k, path in files.items():
+                try:
+                    v = current(path)
+                except OSError:
+                    v = None
+                if v is not None:
+                    samples[k].append(v)
+            done.wait(0.02)
+
+    for _ in range(n_calls):
+        fn()
+    t = threading.Thread(target=sample)
+    t.start()
+    torch.cuda.synchronize()
+    done.set()
+    t.join()
+    out = {"source": dev + "/pp_dpm_{sclk,mclk}, sampled during untimed JVP calls"}
+    for k, v in samples.items():
+        v = sorted(v)
+        out[k + "_mhz"] = ({"min": v[0], "median": v[len(v) // 2], "max": v[-1], "samples": len(v)}
+                           if v else None)
+    return out
+
+
 def cpu_baseline(w, x, target_s=18.0):
     """The fp64 oracle on a bounded sample of the same workload: query rows of
     slice (b=0, h=0) spread over every unit of both streams, sized to about
@@ -213,6 +268,8 @@ def main():
     value = flops / (ms * 1e-3) / 1e12
     log(f"JVP: {ms:.3f} ms/call, {value:.1f} TFLOP/s "
         f"({100 * value / PEAK_BF16_TFLOPS:.1f}% of bf16 peak)")
+    clocks = clock_under_load(jvp)
+    log(f"clocks under load: {clocks}")
     res = {
         "metric": "attention-JVP TFLOP/s (primal+tangent) and % of bf16 MFMA peak, 1 GPU",
         "value": round(value, 2),
@@ -233,6 +290,7 @@ def main():
         "ms_p10": round(per_sorted[len(per) // 10], 4),
         "ms_median": round(per_sorted[len(per) // 2], 4),
         "ms_p90": round(per_sorted[(9 * len(per)) // 10], 4),
+        "gpu_clocks": clocks,
     }
     if not args.no_primal:
         pms, _ = time_calls(primal, args.steps, args.warmup, stream)
