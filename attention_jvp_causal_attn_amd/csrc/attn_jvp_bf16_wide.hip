@@ -225,6 +225,14 @@ __device__ __forceinline__ void issue_block(uint32_t st, int wave, const KernelP
 }
 
 // S^T = K Q^T and dS^T = K dQ^T + dK Q^T; Q from registers, dQ from LDS.
+// Key-loop code shape: every kernel but the head-dim-128 JVP kernel (whose
+// registers are all taken) holds its per-lane LDS read offsets across the key
+// loop and runs the loop unrolled by two, so that each block's ring stage is
+// an immediate offset of those reads (primal kernels -7 %, head-dim-64 JVP
+// kernel -17 %; at head dim 128 the JVP kernel rebuilds the offsets per block).
+template <int D, bool TAN>
+constexpr bool kHoldOffsets = !TAN || D == 64;
+
 template <int D, bool TAN>
 __device__ __forceinline__ void score_block(const StageTile<D> *st, const uint4 *dq_lds,
                                             const bf16x8 *qf, int row_in_tile, f32x16 &S,
@@ -236,10 +244,10 @@ __device__ __forceinline__ void score_block(const StageTile<D> *st, const uint4 
   const uint4 *Ks = st->k + krow * KCH;
   const uint4 *dKs = st->dk + krow * KCH;
   const uint4 *dQs = dq_lds + row_in_tile * KCH;
-  // opaque per call: the per-step addresses are rebuilt each block instead of
-  // being held in registers across the key loop
+  // opaque per call where offsets are not held: the per-step addresses are
+  // then rebuilt each block
   int kx = k_swz<D>(krow), qx = k_swz<D>(row_in_tile);
-  asm volatile("" : "+v"(kx), "+v"(qx));
+  if constexpr (!kHoldOffsets<D, TAN>) asm volatile("" : "+v"(kx), "+v"(qx));
   S = f32x16{};
   dS = f32x16{};
 #pragma unroll
@@ -358,7 +366,7 @@ __device__ __forceinline__ void softmax_value_block(const StageTile<D> *st, f32x
   const int g = lane >> 4, jl = lane & 15;
   int dcol = 16 * (g & 1) + 4 * (jl & 3);
   int krel = 8 * hh + (jl >> 2);
-  asm volatile("" : "+v"(dcol), "+v"(krel));
+  if constexpr (!kHoldOffsets<D, TAN>) asm volatile("" : "+v"(dcol), "+v"(krel));
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
 #pragma unroll
@@ -486,22 +494,46 @@ void attn_jvp_bf16_wide_kernel(KernelParams p) {
   }
   float m_ref = kNegInf, l_run = 0.f, mu_run = 0.f;
 
-  for (int j = 0; j < n; ++j) {
-    if ((j + 2) % kEntChunk == 0 && j + 2 < n) load_entries((j + 2) / kEntChunk);
-    wait_vmcnt<0>();  // block j (and, first time, dQ and Q) has landed
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    const Stage *st = &ring[j & 1];
-    f32x16 S, dS;
-    score_block<D, TAN>(st, dq_lds, qf, row_in_tile, S, dS);
-    // block j + 1 into the other stage (released by the barrier)
-    if (j + 1 < n)
-      issue_block<D, TAN>(stage_lds((j + 1) & 1), wave, p, kb_, dkb_, vb_, dvb_, ent_1.x * BN,
-                       bits_of(ent_1));
-    softmax_value_block<D, TAN>(st, S, dS, accO, accT, m_ref, l_run, mu_run, ent_c.y >= 0,
-                             row_in_tile, p.scale_log2, p.scale);
-    ent_c = ent_1;
-    ent_1 = j + 2 < n ? entry(j + 2) : no_ent;
+  if constexpr (!kHoldOffsets<D, TAN>) {
+    for (int j = 0; j < n; ++j) {
+      if ((j + 2) % kEntChunk == 0 && j + 2 < n) load_entries((j + 2) / kEntChunk);
+      wait_vmcnt<0>();  // block j (and, first time, dQ and Q) has landed
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      const Stage *st = &ring[j & 1];
+      f32x16 S, dS;
+      score_block<D, TAN>(st, dq_lds, qf, row_in_tile, S, dS);
+      // block j + 1 into the other stage (released by the barrier)
+      if (j + 1 < n)
+        issue_block<D, TAN>(stage_lds((j + 1) & 1), wave, p, kb_, dkb_, vb_, dvb_, ent_1.x * BN,
+                         bits_of(ent_1));
+      softmax_value_block<D, TAN>(st, S, dS, accO, accT, m_ref, l_run, mu_run, ent_c.y >= 0,
+                               row_in_tile, p.scale_log2, p.scale);
+      ent_c = ent_1;
+      ent_1 = j + 2 < n ? entry(j + 2) : no_ent;
+    }
+  } else {
+    // the same block loop, unrolled by two: each block's ring stage is an
+    // immediate offset of the (held) per-lane read addresses
+    auto step = [&](int j, const Stage *st, int next_stage) __attribute__((always_inline)) {
+      if ((j + 2) % kEntChunk == 0 && j + 2 < n) load_entries((j + 2) / kEntChunk);
+      wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      f32x16 S, dS;
+      score_block<D, TAN>(st, dq_lds, qf, row_in_tile, S, dS);
+      if (j + 1 < n)
+        issue_block<D, TAN>(stage_lds(next_stage), wave, p, kb_, dkb_, vb_, dvb_, ent_1.x * BN,
+                         bits_of(ent_1));
+      softmax_value_block<D, TAN>(st, S, dS, accO, accT, m_ref, l_run, mu_run, ent_c.y >= 0,
+                               row_in_tile, p.scale_log2, p.scale);
+      ent_c = ent_1;
+      ent_1 = j + 2 < n ? entry(j + 2) : no_ent;
+    };
+    for (int j = 0; j < n; j += 2) {
+      step(j, &ring[0], 1);
+      if (j + 1 < n) step(j + 1, &ring[1], 0);
+    }
   }
 
   const float l_tot = l_run + xor32(l_run);
