@@ -226,10 +226,11 @@ __device__ __forceinline__ void issue_block(uint32_t st, int wave, const KernelP
 
 // S^T = K Q^T and dS^T = K dQ^T + dK Q^T; Q from registers, dQ from LDS.
 // Key-loop code shape: every kernel but the head-dim-128 JVP kernel (whose
-// registers are all taken) holds its per-lane LDS read offsets across the key
-// loop and runs the loop unrolled by two, so that each block's ring stage is
-// an immediate offset of those reads (primal kernels -7 %, head-dim-64 JVP
-// kernel -17 %; at head dim 128 the JVP kernel rebuilds the offsets per block).
+// registers are all taken) holds its per-lane score-phase LDS read offsets
+// across the key loop and runs the loop unrolled by two, so that each block's
+// ring stage is an immediate offset of those reads (primal kernels -7 %,
+// head-dim-64 JVP kernel -17 %; at head dim 128 the JVP kernel rebuilds its
+// score-phase offsets per block).
 template <int D, bool TAN>
 constexpr bool kHoldOffsets = !TAN || D == 64;
 
@@ -379,9 +380,9 @@ __device__ __forceinline__ void softmax_value_block(const StageTile<D> *st, f32x
     if (TAN) mu_run += musum;
   }
   const int g = lane >> 4, jl = lane & 15;
-  int dcol = 16 * (g & 1) + 4 * (jl & 3);
-  int krel = 8 * hh + (jl >> 2);
-  if constexpr (!kHoldOffsets<D, TAN>) asm volatile("" : "+v"(dcol), "+v"(krel));
+  // (held across the key loop by every kernel: these are few)
+  const int dcol = 16 * (g & 1) + 4 * (jl & 3);
+  const int krel = 8 * hh + (jl >> 2);
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
 #pragma unroll
