@@ -159,6 +159,12 @@ template <int D>
 __device__ __forceinline__ bf16x8 row_operand(const uint4 *tile, int prow, int t, int hh) {
   return as_bf16x8(tile[prow * Geo<D>::KCH + ((2 * t + hh) ^ sw<D>(prow))]);
 }
+// The same read as the byte offset 32 t ^ y from the row's start, y = 16 (hh ^
+// sw(row)): one xor-add per read with the step's constant, for a pass that
+// rebuilds its offsets per block.
+__device__ __forceinline__ bf16x8 row_read_xad(const char *row, int t, uint32_t y) {
+  return as_bf16x8(*reinterpret_cast<const uint4 *>(row + ((32u * uint32_t(t)) ^ y)));
+}
 // A-operand transposed read of a swizzled 32 x D tile for step s of 16
 // rows and dim tile nt: within each 16-lane group, lane jl reads row
 // (16s + 4*half + krel) at dims (d0 + 4*(jl%4)) .. +3.
@@ -183,23 +189,14 @@ __device__ __forceinline__ int reg_pos(int r) {
   return 16 * (j >> 1) + 4 * (j & 1) + i;
 }
 
-// Per-lane constants of the transposed reads, opaque so that they are
-// rebuilt per block rather than held across the key loop.
+// Per-lane constants of the transposed reads (held across the key loop).
 struct TrLane {
   int dcol, krel;
 };
-__device__ __forceinline__ TrLane tr_lane_plain() {
-  const int lane = threadIdx.x & 63;
-  const int g = lane >> 4, jl = lane & 15;
-  return {16 * (g & 1) + 4 * (jl & 3), 8 * (lane >> 5) + (jl >> 2)};
-}
 __device__ __forceinline__ TrLane tr_lane() {
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4, jl = lane & 15;
-  int dcol = 16 * (g & 1) + 4 * (jl & 3);
-  int krel = 8 * (lane >> 5) + (jl >> 2);
-  asm volatile("" : "+v"(dcol), "+v"(krel));
-  return {dcol, krel};
+  return {16 * (g & 1) + 4 * (jl & 3), 8 * (lane >> 5) + (jl >> 2)};
 }
 
 // ---------------------------------------------------------------- dQ pass
@@ -291,7 +288,7 @@ void bwd_dq_wide_kernel(BwdParams p) {
   // in this pass); the loop below is unrolled by two so that the ring stage
   // of every read is an immediate offset.
   const int krow = swap_bits23(col);
-  const TrLane tl = tr_lane_plain();
+  const TrLane tl = tr_lane();
   // One block: S^T, dP^T, dS^T and the dQ update.
   auto step = [&](int j, const KVTile *st, int next_stage) __attribute__((always_inline)) {
     if ((j + 1) % kEntChunk == 0 && j + 1 < n) load_entries((j + 1) / kEntChunk);
@@ -454,12 +451,13 @@ void bwd_dkv_wide_kernel(BwdParams p) {
   }
   const float sl2 = p.scale_log2;
 
-  // Per-lane LDS read offsets: held across the key loop at head dim 64;
-  // rebuilt per block at head dim 128, where the registers are all taken.
-  // The loop is unrolled by two as in the dQ pass.
+  // Per-lane LDS read offsets: held across the key loop at head dim 64; at
+  // head dim 128, where registers are short, the row-read offsets are rebuilt
+  // per block (one xor-add per read) and only the transposed-read offsets are
+  // held.  The loop is unrolled by two as in the dQ pass.
   constexpr bool kHoist = D == 64;
   const int qperm_h = swap_bits23(col);
-  const TrLane tl_h = tr_lane_plain();
+  const TrLane tl_h = tr_lane();
   // One block of 32 queries: S, dP, dS and the dK, dV updates.
   auto step = [&](int j, const QGTile *st, int next_stage) __attribute__((always_inline)) {
     if ((j + 1) % kEntChunk == 0 && j + 1 < n) load_entries((j + 1) / kEntChunk);
@@ -474,12 +472,27 @@ void bwd_dkv_wide_kernel(BwdParams p) {
     }
     const uint4 *vrow = v_lds + key_in_tile * KCH;
     f32x16 S = {}, G = {};
+    if constexpr (kHoist) {
 #pragma unroll
-    for (int t = 0; t < KSTEPS; ++t) {
-      const bf16x8 vf = as_bf16x8(vrow[(2 * t + hh) ^ sw<D>(key_in_tile)]);
-      S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(st->q, qperm, t, hh), kf[t], S, 0, 0, 0);
-      G = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(st->g, qperm, t, hh), vf, G, 0, 0, 0);
-      if (t % 4 == 3) __builtin_amdgcn_sched_barrier(0);  // bound the operand prefetch
+      for (int t = 0; t < KSTEPS; ++t) {
+        const bf16x8 vf = as_bf16x8(vrow[(2 * t + hh) ^ sw<D>(key_in_tile)]);
+        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(st->q, qperm, t, hh), kf[t], S, 0, 0, 0);
+        G = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(st->g, qperm, t, hh), vf, G, 0, 0, 0);
+        if (t % 4 == 3) __builtin_amdgcn_sched_barrier(0);  // bound the operand prefetch
+      }
+    } else {
+      uint32_t qy = 16u * uint32_t(hh ^ sw<D>(qperm)), vy = 16u * uint32_t(hh ^ sw<D>(key_in_tile));
+      asm volatile("" : "+v"(qy), "+v"(vy));
+      const char *qrow = reinterpret_cast<const char *>(st->q + qperm * KCH);
+      const char *grow = reinterpret_cast<const char *>(st->g + qperm * KCH);
+      const char *vr = reinterpret_cast<const char *>(vrow);
+#pragma unroll
+      for (int t = 0; t < KSTEPS; ++t) {
+        const bf16x8 vf = row_read_xad(vr, t, vy);
+        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read_xad(qrow, t, qy), kf[t], S, 0, 0, 0);
+        G = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read_xad(grow, t, qy), vf, G, 0, 0, 0);
+        if (t % 4 == 3) __builtin_amdgcn_sched_barrier(0);  // bound the operand prefetch
+      }
     }
     if (j + 1 < n) issue(next_stage, entry(j + 1));  // its stage was released by the barrier
     // LSE and D of this lane's 16 queries 8hh + {0..7} and 16 + 8hh + {0..7}:
@@ -521,7 +534,7 @@ void bwd_dkv_wide_kernel(BwdParams p) {
     pb[1] = to_bf16x8(pr + 8);
     gsb[0] = to_bf16x8(gs);
     gsb[1] = to_bf16x8(gs + 8);
-    const TrLane tl = kHoist ? tl_h : tr_lane();
+    const TrLane tl = tl_h;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
 #pragma unroll
