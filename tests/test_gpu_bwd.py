@@ -149,6 +149,34 @@ def test_full_size_batched_workload_bwd_sampled():
     check("D", f64(delta[b:b + 1, h:h + 1, rows]), Ds)
 
 
+@pytest.mark.parametrize("D", [64])
+def test_chunkwise_11k_bwd_sampled(D):
+    # 7 chunks of 3 frames x 520 tokens per stream (N = 21,840 with the clean
+    # and noisy streams: 86 query tiles), one (b, h) slice checked on sampled
+    # rows (dQ) and sampled keys (dK, dV), chunk boundaries included (head
+    # dim 128 has the batched 22k case)
+    nf, tpf, fpc, H = 21, 520, 3, 2
+    pred = tf_allowed(nf, tpf, fpc)
+    say(f"case: bwd chunk-wise TF nf={nf} tpf={tpf} fpc={fpc} H={H} D={D} (N={pred.n_q})")
+    x = make_random(1, pred.n_q, H, D, dtype="bf16", seed=6400 + D)
+    g = make_random(1, pred.n_q, H, D, dtype="bf16", seed=6401 + D)["q"]
+    mask = aj.attn_jvp_mask_tf(nf, tpf, fpc)
+    gq, gk, gv, delta = run_bwd(x, g, mask)
+    C, Nc = tpf * fpc, nf * tpf
+    edges = {s + u * C + o for s in (0, Nc) for u in range(nf // fpc) for o in (0, C - 1)}
+    rng = np.random.default_rng(D)
+    rows = np.array(sorted(edges | set(rng.integers(0, pred.n_q, size=24).tolist())))
+    keys = np.array(sorted(edges | set(rng.integers(0, pred.n_q, size=24).tolist())))
+    h = 1
+    sl = {k: v[:, :, h:h + 1] for k, v in x.items()}
+    dQ, dK, dV, Ds = masked_attention_grad(sl["q"], sl["k"], sl["v"], g[:, :, h:h + 1], pred,
+                                           rows=rows, keys=keys, row_block=256)
+    check("dQ", f64(gq[:, rows, h:h + 1]), dQ)
+    check("dK", f64(gk[:, keys, h:h + 1]), dK)
+    check("dV", f64(gv[:, keys, h:h + 1]), dV)
+    check("D", f64(delta[:, h:h + 1, rows]), Ds)
+
+
 # ------------------------------------------------------------ fp32 path ----
 
 @pytest.mark.parametrize("D", [64, 128])

@@ -9,6 +9,7 @@ the GPU sees (bf16 and fp32 widen to fp64 exactly).
 import math
 import os
 import sys
+import types
 
 import numpy as np
 import pytest
@@ -404,6 +405,20 @@ def test_full_size_workload_sampled(wid):
     rows = sample_rows(w, seed=wid)
     say(f"  {len(rows)} sampled rows per (b, h)")
     parity(x, pred, mask, TOL[torch.bfloat16], rows=rows)
+
+
+def test_head_dim_64_long_sequence_sampled():
+    # the chunk-wise 65,520-token sequence at head dim 64 (4 heads), sampled
+    # rows of every (b, h)
+    nf, tpf, fpc, H, D = 21, 1560, 3, 4, 64
+    pred = tf_allowed(nf, tpf, fpc)
+    say(f"case: chunk-wise TF nf={nf} tpf={tpf} fpc={fpc} H={H} D={D} (N={pred.n_q})")
+    x = make_random(1, pred.n_q, H, D, dtype="bf16", seed=6464, tangent_std=0.1)
+    w = types.SimpleNamespace(n_frames=nf, tokens_per_frame=tpf, unit_tokens=tpf * fpc,
+                              n_units=nf // fpc, N=pred.n_q)
+    rows = sample_rows(w, seed=64)
+    say(f"  {len(rows)} sampled rows per (b, h)")
+    parity(x, pred, aj.attn_jvp_mask_tf(nf, tpf, fpc), TOL[torch.bfloat16], rows=rows)
 
 
 def test_rows_beyond_4gib_of_one_slice():
