@@ -409,7 +409,10 @@ __device__ __forceinline__ void softmax_value_block(const StageTile<D> *st, f32x
         accT[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pdsb[s], accT[nt], 0, 0, 0);
         accT[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dvf, pb[s], accT[nt], 0, 0, 0);
       }
-      if (nt % 2 == 1) __builtin_amdgcn_sched_barrier(0);  // bound the operand prefetch
+      // bound the operand prefetch: every two dim tiles, or at head dim 128
+      // with tangents every four (0.4 % faster there)
+      constexpr int kFence = (D == 128 && TAN) ? 4 : 2;
+      if (nt % kFence == kFence - 1) __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
