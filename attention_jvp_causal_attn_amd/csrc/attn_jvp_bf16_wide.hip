@@ -326,59 +326,36 @@ __device__ __forceinline__ void softmax_value_block(const StageTile<D> *st, f32x
   const float m_use = m_ref == kNegInf ? 0.f : m_ref;
   float pr[16], pds[16];
   bf16x8 pb[2], pdsb[2];
-  if constexpr (D == 128) {
-    // l and mu summed from the fp32 weights
-    float lsum = 0.f, musum = 0.f;
+  // l and mu are summed from the bf16 weights the value MFMAs consume, two
+  // per v_dot2 (half the vector instructions of fp32 sums, and O, dO are then
+  // normalised by exactly the weights they were accumulated with)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], scale_log2, -m_use));
-      lsum += pr[r];
-      if (TAN) {
-        const float dss = dS[r] * scale;
-        pds[r] = pr[r] * dss;
-        musum = __builtin_fmaf(pr[r], dss, musum);
-      }
-    }
-    l_run += lsum;
-    if (TAN) mu_run += musum;
-    pb[0] = to_bf16x8(pr);
-    pb[1] = to_bf16x8(pr + 8);
-    if (TAN) {
-      pdsb[0] = to_bf16x8(pds);
-      pdsb[1] = to_bf16x8(pds + 8);
-    }
-  } else {
-    // head dim 64: l and mu summed from the bf16 weights the value MFMAs
-    // consume, two per v_dot2 (half the vector instructions of fp32 sums;
-    // 3 % faster here, 1 % slower at head dim 128)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], scale_log2, -m_use));
-      if (TAN) pds[r] = pr[r] * (dS[r] * scale);
-    }
-    pb[0] = to_bf16x8(pr);
-    pb[1] = to_bf16x8(pr + 8);
-    if (TAN) {
-      pdsb[0] = to_bf16x8(pds);
-      pdsb[1] = to_bf16x8(pds + 8);
-    }
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-    float lsum = 0.f, musum = 0.f;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bf16x2 pp = {pb[h][2 * i], pb[h][2 * i + 1]};
-        lsum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lsum, false);
-        if (TAN) {
-          const bf16x2 qq = {pdsb[h][2 * i], pdsb[h][2 * i + 1]};
-          musum = __builtin_amdgcn_fdot2_f32_bf16(qq, ones, musum, false);
-        }
-      }
-    }
-    l_run += lsum;
-    if (TAN) mu_run += musum;
+  for (int r = 0; r < 16; ++r) {
+    pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], scale_log2, -m_use));
+    if (TAN) pds[r] = pr[r] * (dS[r] * scale);
   }
+  pb[0] = to_bf16x8(pr);
+  pb[1] = to_bf16x8(pr + 8);
+  if (TAN) {
+    pdsb[0] = to_bf16x8(pds);
+    pdsb[1] = to_bf16x8(pds + 8);
+  }
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  float lsum = 0.f, musum = 0.f;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bf16x2 pp = {pb[h][2 * i], pb[h][2 * i + 1]};
+      lsum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lsum, false);
+      if (TAN) {
+        const bf16x2 qq = {pdsb[h][2 * i], pdsb[h][2 * i + 1]};
+        musum = __builtin_amdgcn_fdot2_f32_bf16(qq, ones, musum, false);
+      }
+    }
+  }
+  l_run += lsum;
+  if (TAN) mu_run += musum;
   const int g = lane >> 4, jl = lane & 15;
   // (held across the key loop by every kernel: these are few)
   const int dcol = 16 * (g & 1) + 4 * (jl & 3);
