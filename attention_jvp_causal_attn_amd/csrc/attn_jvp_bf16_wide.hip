@@ -225,19 +225,19 @@ __device__ __forceinline__ void issue_block(uint32_t st, int wave, const KernelP
 }
 
 // S^T = K Q^T and dS^T = K dQ^T + dK Q^T; Q from registers, dQ from LDS.
-// Key-loop code shape: every kernel but the head-dim-128 JVP kernel (whose
-// registers are all taken) holds its per-lane score-phase LDS read offsets
+// Key-loop code shape: every kernel holds its per-lane LDS read offsets
 // across the key loop and runs the loop unrolled by two, so that each block's
 // ring stage is an immediate offset of those reads (primal kernels -7 %,
-// head-dim-64 JVP kernel -17 %; at head dim 128 the JVP kernel rebuilds its
-// score-phase offsets per block).
+// head-dim-64 JVP kernel -17 %, head-dim-128 JVP kernel -3 %).  The
+// head-dim-128 JVP kernel writes its score-phase row reads as one xor-add
+// each (below), which is what leaves it the registers to do so.
 template <int D, bool TAN>
-constexpr bool kHoldOffsets = !TAN || D == 64;
+constexpr bool kXadReads = D == 128 && TAN;
 
-// Row-operand read of chunk (2t + hh) ^ x of a row.  Where offsets are
-// rebuilt per block it is written as the byte offset 32 t ^ y, y = 16 (hh ^
-// x): one xor-add per read with the step's constant (1.3 % faster there, 1 %
-// slower where offsets are held).
+// Row-operand read of chunk (2t + hh) ^ x of a row, as an index or as the
+// byte offset 32 t ^ y, y = 16 (hh ^ x): one xor-add per read with the step's
+// constant (fewer vector instructions and registers in the head-dim-128 JVP
+// kernel; 1 % slower in the head-dim-64 one).
 template <bool XAD>
 __device__ __forceinline__ bf16x8 row_read(const uint4 *row, int t, int hh, int x, uint32_t y) {
   if constexpr (XAD)
@@ -258,12 +258,9 @@ __device__ __forceinline__ void score_block(const StageTile<D> *st, const uint4 
   const uint4 *Ks = st->k + krow * KCH;
   const uint4 *dKs = st->dk + krow * KCH;
   const uint4 *dQs = dq_lds + row_in_tile * KCH;
-  // opaque per call where offsets are not held: the per-step addresses are
-  // then rebuilt each block
-  constexpr bool kXad = !kHoldOffsets<D, TAN>;
+  constexpr bool kXad = kXadReads<D, TAN>;
   const int kx = k_swz<D>(krow), qx = k_swz<D>(row_in_tile);
-  uint32_t ky = 16u * uint32_t(hh ^ kx), qy = 16u * uint32_t(hh ^ qx);
-  if constexpr (kXad) asm volatile("" : "+v"(ky), "+v"(qy));
+  const uint32_t ky = 16u * uint32_t(hh ^ kx), qy = 16u * uint32_t(hh ^ qx);
   S = f32x16{};
   dS = f32x16{};
 #pragma unroll
@@ -490,34 +487,17 @@ void attn_jvp_bf16_wide_kernel(KernelParams p) {
   }
   float m_ref = kNegInf, l_run = 0.f, mu_run = 0.f;
 
-  if constexpr (!kHoldOffsets<D, TAN>) {
-    for (int j = 0; j < n; ++j) {
+  {
+    // the block loop, unrolled by two: each block's ring stage is an
+    // immediate offset of the (held) per-lane read addresses
+    auto step = [&](int j, const Stage *st, int next_stage) __attribute__((always_inline)) {
       if ((j + 2) % kEntChunk == 0 && j + 2 < n) load_entries((j + 2) / kEntChunk);
       wait_vmcnt<0>();  // block j (and, first time, dQ and Q) has landed
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
-      const Stage *st = &ring[j & 1];
       f32x16 S, dS;
       score_block<D, TAN>(st, dq_lds, qf, row_in_tile, S, dS);
       // block j + 1 into the other stage (released by the barrier)
-      if (j + 1 < n)
-        issue_block<D, TAN>(stage_lds((j + 1) & 1), wave, p, kb_, dkb_, vb_, dvb_, ent_1.x * BN,
-                         bits_of(ent_1));
-      softmax_value_block<D, TAN>(st, S, dS, accO, accT, m_ref, l_run, mu_run, ent_c.y >= 0,
-                               row_in_tile, p.scale_log2, p.scale);
-      ent_c = ent_1;
-      ent_1 = j + 2 < n ? entry(j + 2) : no_ent;
-    }
-  } else {
-    // the same block loop, unrolled by two: each block's ring stage is an
-    // immediate offset of the (held) per-lane read addresses
-    auto step = [&](int j, const Stage *st, int next_stage) __attribute__((always_inline)) {
-      if ((j + 2) % kEntChunk == 0 && j + 2 < n) load_entries((j + 2) / kEntChunk);
-      wait_vmcnt<0>();
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-      f32x16 S, dS;
-      score_block<D, TAN>(st, dq_lds, qf, row_in_tile, S, dS);
       if (j + 1 < n)
         issue_block<D, TAN>(stage_lds(next_stage), wave, p, kb_, dkb_, vb_, dvb_, ent_1.x * BN,
                          bits_of(ent_1));
