@@ -273,9 +273,10 @@ __device__ __forceinline__ void score_block(const StageTile<D> *st, const uint4 
       dS = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, dqf, dS, 0, 0, 0);
       dS = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dkf, qf[t], dS, 0, 0, 0);
     }
-    // bound the operand prefetch to four k-steps (measured: two steps ahead
-    // exposes more LDS latency, no bound spills)
-    if (t % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+    // bound the operand prefetch: four k-steps (no bound spills), or two in
+    // the head-dim-128 JVP kernel (0.5 % faster there)
+    constexpr int kFence = (D == 128 && TAN) ? 2 : 4;
+    if (t % kFence == kFence - 1) __builtin_amdgcn_sched_barrier(0);
   }
 }
 
