@@ -224,7 +224,6 @@ __device__ __forceinline__ void issue_block(uint32_t st, int wave, const KernelP
           st + uint32_t(offsetof(StageTile<D>, bits)) + uint32_t(wave) * 128u);
 }
 
-// S^T = K Q^T and dS^T = K dQ^T + dK Q^T; Q from registers, dQ from LDS.
 // Key-loop code shape: every kernel holds its per-lane LDS read offsets
 // across the key loop and runs the loop unrolled by two, so that each block's
 // ring stage is an immediate offset of those reads (primal kernels -7 %,
@@ -247,6 +246,7 @@ __device__ __forceinline__ bf16x8 row_read(const uint4 *row, int t, int hh, int 
     return as_bf16x8(row[(2 * t + hh) ^ x]);
 }
 
+// S^T = K Q^T and dS^T = K dQ^T + dK Q^T; Q from registers, dQ from LDS.
 template <int D, bool TAN>
 __device__ __forceinline__ void score_block(const StageTile<D> *st, const uint4 *dq_lds,
                                             const bf16x8 *qf, int row_in_tile, f32x16 &S,
