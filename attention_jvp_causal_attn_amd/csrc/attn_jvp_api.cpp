@@ -349,8 +349,10 @@ extern "C" int attn_jvp_split_choose(const attn_jvp_args *a, const attn_jvp_mask
   int BM = 0, BN = 0;
   attn_jvp_tile_shape(a->dtype, a->D, &BM, &BN);
   // workgroups resident per compute unit: one for the bf16 kernels (their
-  // registers fill the SIMDs), two for the fp32 kernel
-  const int64_t slots = int64_t(n_cu) * (a->dtype == ATTN_JVP_BF16 ? 1 : 2);
+  // registers fill the SIMDs) but the head-dim-64 primal one (four waves per
+  // SIMD: two), two for the fp32 kernel
+  const bool two = a->dtype != ATTN_JVP_BF16 || (!tangent && a->D == 64);
+  const int64_t slots = int64_t(n_cu) * (two ? 2 : 1);
   const int64_t slices = int64_t(a->B) * a->H;
   std::lock_guard<std::mutex> lock(m->mu);
   const attnjvp::HostSplit *h1 = attnjvp::host_split_locked(m, BM, BN, 1, &st);
