@@ -70,7 +70,7 @@ def parity(x, pred, mask, S, dtype, rows=None):
 
 CASES = [  # dtype, D, TF (nf, tpf, fpc), B, H
     ("bf16", 128, (5, 137, 1), 1, 2),   # N = 1370: 6 tiles of 256 rows, ragged tail
-    ("bf16", 64, (6, 93, 2), 2, 1),     # 128-row tiles
+    ("bf16", 64, (6, 93, 2), 2, 1),     # N = 1116: 5 tiles of 256 rows, ragged tail
     ("f32", 64, (4, 70, 2), 1, 2),      # 64-row tiles, natural-log partials
     ("f32", 128, (3, 50, 1), 1, 1),
 ]
