@@ -146,6 +146,12 @@ __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
+// s_waitcnt lgkmcnt(0): this wave's LDS writes are done, so a following
+// s_barrier publishes them to the workgroup (the compiler adds no such wait
+// before a bare s_barrier).
+__device__ __forceinline__ void wait_lgkmcnt0() {
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
+}
 
 // A zero row: the copy source of an absent (zero) tangent tensor, read with
 // row-independent offsets.
@@ -499,7 +505,11 @@ void attn_jvp_bf16_wide_kernel(KernelParams p) {
     // the block loop, unrolled by two: each block's ring stage is an
     // immediate offset of the (held) per-lane read addresses
     auto step = [&](int j, const Stage *st, int next_stage) __attribute__((always_inline)) {
-      if ((j + 2) % kEntChunk == 0 && j + 2 < n) load_entries((j + 2) / kEntChunk);
+      if ((j + 2) % kEntChunk == 0 && j + 2 < n) {
+        // the next chunk of entries, read after this barrier (entry(j + 2))
+        load_entries((j + 2) / kEntChunk);
+        wait_lgkmcnt0();
+      }
       wait_vmcnt<0>();  // block j (and, first time, dQ and Q) has landed
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");

@@ -117,6 +117,12 @@ __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
+// s_waitcnt lgkmcnt(0): this wave's LDS writes are done, so a following
+// s_barrier publishes them to the workgroup (the compiler adds no such wait
+// before a bare s_barrier).
+__device__ __forceinline__ void wait_lgkmcnt0() {
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
+}
 
 // Byte offset of chunk q of a 32-row block (swizzled); rows past the last
 // valid one re-read it (masked out by the schedule).
@@ -297,7 +303,11 @@ void bwd_dq_wide_kernel(BwdParams p) {
   const TrLane tl = tr_lane();
   // One block: S^T, dP^T, dS^T and the dQ update.
   auto step = [&](int j, const KVTile *st, int next_stage) __attribute__((always_inline)) {
-    if ((j + 1) % kEntChunk == 0 && j + 1 < n) load_entries((j + 1) / kEntChunk);
+    if ((j + 1) % kEntChunk == 0 && j + 1 < n) {
+      // the next chunk of entries, read after this barrier (entry(j + 1))
+      load_entries((j + 1) / kEntChunk);
+      wait_lgkmcnt0();
+    }
     wait_vmcnt<0>();  // block j (and, first time, Q, g, O) has landed
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
@@ -466,7 +476,11 @@ void bwd_dkv_wide_kernel(BwdParams p) {
   const TrLane tl_h = tr_lane();
   // One block of 32 queries: S, dP, dS and the dK, dV updates.
   auto step = [&](int j, const QGTile *st, int next_stage) __attribute__((always_inline)) {
-    if ((j + 1) % kEntChunk == 0 && j + 1 < n) load_entries((j + 1) / kEntChunk);
+    if ((j + 1) % kEntChunk == 0 && j + 1 < n) {
+      // the next chunk of entries, read after this barrier (entry(j + 1))
+      load_entries((j + 1) / kEntChunk);
+      wait_lgkmcnt0();
+    }
     wait_vmcnt<0>();  // block j (and, first time, V and K) has landed
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");

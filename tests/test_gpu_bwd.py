@@ -231,3 +231,20 @@ def test_rect_bwd_bf16_unseen_keys_and_empty_rows(D):
     assert torch.all(gq[:, 250:330] == 0) and torch.all(gk[:, 520:] == 0) and torch.all(gv[:, 520:] == 0)
     assert torch.all(delta[:, :, 250:330] == 0)
     parity(x, g, pred, mask)
+
+
+# More than 1,024 blocks of 32 along one tile's list in each pass: 40,017
+# keys per query tile (dQ pass), then 40,017 queries per key tile (dK/dV
+# pass); the entry list is restaged in LDS twice on the way.  Dense masks with
+# a ragged last block, every element compared with the oracle.
+@pytest.mark.parametrize("D", [128, 64])
+@pytest.mark.parametrize("n_q,n_k", [(300, 40017), (40017, 300)])
+def test_long_lists_cross_entry_refills_bwd(n_q, n_k, D):
+    H = 2
+    say(f"case: bwd dense bf16 n_q={n_q} n_k={n_k} H={H} D={D}")
+    pred = dense_allowed(n_q, n_k)
+    xq = make_random(1, n_q, H, D, dtype="bf16", seed=14300 + D)
+    xk = make_random(1, n_k, H, D, dtype="bf16", seed=14400 + D)
+    x = {"q": xq["q"], "k": xk["k"], "v": xk["v"]}
+    g = xq["dq"]
+    parity(x, g, pred, aj.attn_jvp_mask_dense(n_q, n_k))

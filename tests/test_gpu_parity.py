@@ -495,3 +495,37 @@ def test_head_major_memory_layout(dtype, D):
     check("dQ", f64(gq), dQ, tol)
     check("dK", f64(gk), dK, tol)
     check("dV", f64(gv), dV, tol)
+
+
+# A query tile whose key list holds more than two chunks of schedule entries
+# (more than 1,024 key blocks of 32): the kernels restage the entry list in
+# LDS while they walk it, so every refill is crossed here.  Dense masks with a
+# ragged last key block, every element compared with the oracle.
+@pytest.mark.parametrize("D", [128, 64])
+@pytest.mark.parametrize("tangent", [True, False])
+def test_long_key_list_crosses_entry_refills(D, tangent):
+    n_q, n_k, H = 300, 40017, 2
+    say(f"case: dense bf16 n_q={n_q} n_k={n_k} H={H} D={D} tangent={tangent}")
+    pred = dense_allowed(n_q, n_k)
+    xq = make_random(1, n_q, H, D, dtype="bf16", seed=14100 + D, tangent_std=0.1)
+    xk = make_random(1, n_k, H, D, dtype="bf16", seed=14200 + D, tangent_std=0.1)
+    x = dict(q=xq["q"], dq=xq["dq"], k=xk["k"], v=xk["v"], dk=xk["dk"], dv=xk["dv"])
+    xd = to_dev(x)
+    mask = aj.attn_jvp_mask_dense(n_q, n_k)
+    o = torch.full_like(xd["q"], float("nan"))
+    do = torch.full_like(xd["q"], float("nan"))
+    lse = torch.full((1, H, n_q), float("nan"), dtype=torch.float32, device=DEV)
+    if tangent:
+        aj.attn_jvp_fwd(xd["q"], xd["k"], xd["v"], xd["dq"], xd["dk"], xd["dv"], mask, o=o,
+                        d_o=do, lse=lse)
+    else:
+        aj.attn_jvp_fwd(xd["q"], xd["k"], xd["v"], None, None, None, mask, o=o, lse=lse)
+    torch.cuda.synchronize()
+    tol = TOL[torch.bfloat16]
+    if tangent:
+        O, dO, LSE = masked_attention_jvp(x["q"], x["k"], x["v"], x["dq"], x["dk"], x["dv"], pred)
+        check("dO", f64(do), dO, tol)
+    else:
+        O, LSE = masked_attention(x["q"], x["k"], x["v"], pred)
+    check("O", f64(o), O, tol)
+    check("LSE", f64(lse), LSE, tol)
