@@ -99,6 +99,11 @@ def attn_jvp_mask_rects(n_q, n_k, group_q_begin, range_ptr, k_begin, k_end):
     ke, ke_p = _i32arr(k_end)
     if len(rp) != len(gq) or len(kb) != len(ke):
         raise ValueError("group_q_begin/range_ptr and k_begin/k_end lengths must match")
+    # the C builder reads k_begin/k_end[range_ptr[g] .. range_ptr[g + 1]) (after
+    # checking that range_ptr starts at 0 and does not decrease): every pointer
+    # must stay inside the arrays given here
+    if len(rp) < 1 or np.any(rp < 0) or np.any(rp > len(kb)):
+        raise ValueError(f"range_ptr entries must lie in [0, {len(kb)}] (len(k_begin))")
     return _new_mask(L.attn_jvp_mask_rects, int(n_q), int(n_k), len(gq) - 1, gq_p, rp_p,
                      kb_p if len(kb) else None, ke_p if len(ke) else None)
 
@@ -295,9 +300,16 @@ def _shape_args(q, k, tangent):
     """Arguments carrying only the shapes and strides of q and k (for the
     host-only queries: the pointers are placeholders, never dereferenced)."""
     B, n_q, H, D = q.shape
-    fake = 1 << 20
+    n_k = k.shape[1]
+    es = q.element_size()
+
+    def span(t, rows):  # bytes from the first to past the last element of a view
+        return ((B - 1) * abs(t.stride(0)) + (rows - 1) * abs(t.stride(1)) +
+                (H - 1) * abs(t.stride(2)) + D) * es
+    # placeholders far enough apart that no two of them share a byte
+    fake = (max(span(q, n_q), span(k, n_k), B * H * n_q * 4) + 0xfff) & ~0xfff
     return _lib.AttnJvpArgs(
-        dtype=_dtype_code(q), B=B, H=H, n_q=n_q, n_k=k.shape[1], D=D,
+        dtype=_dtype_code(q), B=B, H=H, n_q=n_q, n_k=n_k, D=D,
         q=fake, k=2 * fake, v=3 * fake, dq=4 * fake if tangent else None,
         o=5 * fake, d_o=6 * fake, lse=7 * fake,
         q_stride_b=q.stride(0), q_stride_n=q.stride(1), q_stride_h=q.stride(2),

@@ -15,6 +15,147 @@ namespace {
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// The bytes a strided tensor view covers: base + sum_k i_k * stride_k + e with
+// 0 <= i_k < count_k and 0 <= e < width (the contiguous last dimension), all
+// in bytes.  A contiguous buffer is a view without strided dimensions.
+struct Extent {
+  const void *base = nullptr;
+  int n = 0;
+  int64_t stride[3] = {0, 0, 0};
+  int64_t count[3] = {1, 1, 1};
+  int64_t width = 0;
+};
+
+Extent view_extent(const void *p, int64_t B, int64_t N, int64_t H, int64_t sb, int64_t sn,
+                   int64_t sh, int64_t D, int64_t es) {
+  Extent e;
+  e.base = p;
+  e.n = 3;
+  e.stride[0] = sb * es; e.count[0] = B;
+  e.stride[1] = sn * es; e.count[1] = N;
+  e.stride[2] = sh * es; e.count[2] = H;
+  e.width = D * es;
+  return e;
+}
+
+Extent range_extent(const void *p, int64_t bytes) {
+  Extent e;
+  e.base = p;
+  e.width = bytes;
+  return e;
+}
+
+// Is some sum of c_k x_k, with lo_k <= x_k <= hi_k, inside [L, U] (and, with
+// nonzero, some x_k != 0)?  Depth-first over the terms in decreasing |c|, each
+// term's digits limited to those the remaining terms can still complete; a
+// search that exceeds its node budget answers yes (the caller then refuses).
+struct Term {
+  __int128 c;
+  int64_t lo, hi;
+};
+
+bool reachable(const Term *t, int n, __int128 L, __int128 U, bool nonzero, int64_t *budget) {
+  if (--*budget < 0) return true;
+  if (n == 0) return !nonzero && L <= 0 && 0 <= U;
+  __int128 rmin = 0, rmax = 0;  // what terms 1 .. n-1 can add
+  for (int k = 1; k < n; ++k) {
+    const __int128 a = t[k].c * t[k].lo, b = t[k].c * t[k].hi;
+    rmin += a < b ? a : b;
+    rmax += a < b ? b : a;
+  }
+  // c x in [L - rmax, U - rmin]
+  const __int128 c = t[0].c, lo_v = L - rmax, hi_v = U - rmin;
+  auto fdiv = [](__int128 a, __int128 b) {  // floor(a / b), b > 0
+    __int128 q = a / b;
+    return (a % b != 0 && a < 0) ? q - 1 : q;
+  };
+  __int128 x0, x1;
+  if (c > 0) {
+    x0 = -fdiv(-lo_v, c);  // ceil(lo_v / c)
+    x1 = fdiv(hi_v, c);
+  } else {
+    x0 = -fdiv(hi_v, -c);  // ceil(hi_v / c) for c < 0
+    x1 = fdiv(-lo_v, -c);
+  }
+  if (x0 < t[0].lo) x0 = t[0].lo;
+  if (x1 > t[0].hi) x1 = t[0].hi;
+  for (__int128 x = x0; x <= x1; ++x)
+    if (reachable(t + 1, n - 1, L - c * x, U - c * x, nonzero && x == 0, budget)) return true;
+  return false;
+}
+
+// Normalises the terms (positive coefficients, fixed terms folded into the
+// target, terms of equal coefficient merged: x + y over two ranges takes
+// every value of the summed range) and runs the search.  Only for the
+// existence of a solution, so not with the nonzero condition.
+bool search(std::vector<Term> terms, __int128 L, __int128 U) {
+  std::vector<Term> live;
+  for (Term t : terms) {
+    if (t.c < 0) t = {-t.c, -t.hi, -t.lo};
+    if (t.c == 0 || t.hi == t.lo) {
+      L -= t.c * t.lo;
+      U -= t.c * t.lo;
+      continue;
+    }
+    bool merged = false;
+    for (Term &u : live)
+      if (u.c == t.c) {
+        u.lo += t.lo;
+        u.hi += t.hi;
+        merged = true;
+      }
+    if (!merged) live.push_back(t);
+  }
+  std::sort(live.begin(), live.end(), [](const Term &a, const Term &b) { return a.c > b.c; });
+  int64_t budget = 1 << 20;
+  return reachable(live.data(), int(live.size()), L, U, false, &budget);
+}
+
+// Do two extents share a byte?  (Exact unless the search budget runs out,
+// which answers yes.)
+bool extents_overlap(const Extent &a, const Extent &b) {
+  if (!a.base || !b.base || a.width <= 0 || b.width <= 0) return false;
+  std::vector<Term> t;
+  for (int k = 0; k < a.n; ++k) t.push_back({a.stride[k], 0, a.count[k] - 1});
+  for (int k = 0; k < b.n; ++k) t.push_back({-__int128(b.stride[k]), 0, b.count[k] - 1});
+  const __int128 d = __int128(reinterpret_cast<uintptr_t>(b.base)) -
+                     __int128(reinterpret_cast<uintptr_t>(a.base));
+  // a + sa + e == b + sb + f  <=>  sa - sb == d + f - e, f - e in (-wa, wb)
+  return search(t, d - (a.width - 1), d + (b.width - 1));
+}
+
+// Do two different index tuples of one extent share a byte (a view that
+// writes some element twice)?
+bool extent_self_overlaps(const Extent &a) {
+  if (!a.base || a.width <= 0) return false;
+  std::vector<Term> t;
+  for (int k = 0; k < a.n; ++k) {
+    if (a.count[k] < 2) continue;
+    const int64_t c = a.stride[k] < 0 ? -a.stride[k] : a.stride[k];
+    // a zero stride, or two strides of one size, give one address twice
+    if (c == 0) return true;
+    for (const Term &u : t)
+      if (u.c == c) return true;
+    t.push_back({c, -(a.count[k] - 1), a.count[k] - 1});
+  }
+  std::sort(t.begin(), t.end(), [](const Term &x, const Term &y) { return x.c > y.c; });
+  int64_t budget = 1 << 20;
+  return reachable(t.data(), int(t.size()), -(a.width - 1), a.width - 1, true, &budget);
+}
+
+// Outputs must not share a byte with any input, with another output or with
+// themselves (a write race or a read of a value being overwritten).
+int check_disjoint(const Extent *ins, int n_in, const Extent *outs, int n_out) {
+  for (int i = 0; i < n_out; ++i) {
+    if (extent_self_overlaps(outs[i])) return ATTN_JVP_ERR_UNSUPPORTED;
+    for (int j = 0; j < n_in; ++j)
+      if (extents_overlap(outs[i], ins[j])) return ATTN_JVP_ERR_UNSUPPORTED;
+    for (int j = i + 1; j < n_out; ++j)
+      if (extents_overlap(outs[i], outs[j])) return ATTN_JVP_ERR_UNSUPPORTED;
+  }
+  return ATTN_JVP_OK;
+}
+
 // Upload (once per device and tile shape) the schedule of m; caller holds m->mu.
 int device_schedule_locked(const attn_jvp_mask *m, int device, int BM, int BN,
                            const DeviceSchedule **out) {
@@ -226,14 +367,22 @@ static int validate_fwd(const attn_jvp_args *a, const attn_jvp_mask *m, bool *ta
   for (const void *p : outs)
     if (p && !aligned16(p)) return ATTN_JVP_ERR_ALIGN;
   if (a->d_lse && !tangent) return ATTN_JVP_ERR_UNSUPPORTED;
-  for (const void *p : ins)
-    for (const void *o : outs)
-      if (p && o && p == o) return ATTN_JVP_ERR_UNSUPPORTED;
-  const int n_out = tangent ? 4 : 2;  // o, lse always; d_o and d_lse with a tangent
-  const void *live[4] = {a->o, a->lse, a->d_o, a->d_lse};
-  for (int i = 0; i < n_out; ++i)
-    for (int j = i + 1; j < n_out; ++j)
-      if (live[i] && live[i] == live[j]) return ATTN_JVP_ERR_UNSUPPORTED;
+  // no output may share a byte with an input or another output
+  const Extent in_ext[6] = {
+      view_extent(a->q, a->B, a->n_q, a->H, qs[0], qs[1], qs[2], a->D, es),
+      view_extent(a->dq, a->B, a->n_q, a->H, qs[0], qs[1], qs[2], a->D, es),
+      view_extent(a->k, a->B, a->n_k, a->H, ks[0], ks[1], ks[2], a->D, es),
+      view_extent(a->v, a->B, a->n_k, a->H, ks[0], ks[1], ks[2], a->D, es),
+      view_extent(a->dk, a->B, a->n_k, a->H, ks[0], ks[1], ks[2], a->D, es),
+      view_extent(a->dv, a->B, a->n_k, a->H, ks[0], ks[1], ks[2], a->D, es)};
+  const int64_t lse_bytes = int64_t(a->B) * a->H * a->n_q * 4;
+  const Extent out_ext[4] = {
+      view_extent(a->o, a->B, a->n_q, a->H, qs[0], qs[1], qs[2], a->D, es),
+      range_extent(a->lse, lse_bytes),
+      view_extent(tangent ? a->d_o : nullptr, a->B, a->n_q, a->H, qs[0], qs[1], qs[2], a->D, es),
+      range_extent(tangent ? a->d_lse : nullptr, lse_bytes)};
+  const int st = check_disjoint(in_ext, 6, out_ext, 4);
+  if (st != ATTN_JVP_OK) return st;
   *tangent_out = tangent;
   return ATTN_JVP_OK;
 }
@@ -404,14 +553,25 @@ extern "C" int attn_jvp_fwd_split(const attn_jvp_args *a, const attn_jvp_mask *m
   const int64_t slices = int64_t(a->B) * a->H;
   if (n_units * slices > int64_t(0x7fffffff) || n_split * slices * BM > int64_t(0x7fffffff))
     return ATTN_JVP_ERR_SHAPE;
-  if (workspace) {
-    // the workspace must not overlap a tensor the launch reads or writes
-    const uintptr_t w0 = reinterpret_cast<uintptr_t>(workspace), w1 = w0 + uint64_t(need);
-    const void *ptrs[10] = {a->q, a->k, a->v, a->dq, a->dk, a->dv, a->o, a->d_o, a->lse, a->d_lse};
-    for (const void *q : ptrs) {
-      const uintptr_t x = reinterpret_cast<uintptr_t>(q);
-      if (q && x >= w0 && x < w1) return ATTN_JVP_ERR_UNSUPPORTED;
+  if (workspace && need > 0) {
+    // the workspace must not share a byte with a tensor the launch reads or
+    // writes
+    const int64_t es = a->dtype == ATTN_JVP_BF16 ? 2 : 4;
+    const int64_t lse_bytes = int64_t(a->B) * a->H * a->n_q * 4;
+    const void *qside[4] = {a->q, a->dq, a->o, tangent ? a->d_o : nullptr};
+    const void *kside[4] = {a->k, a->v, a->dk, a->dv};
+    Extent t[10];
+    for (int i = 0; i < 4; ++i) {
+      t[i] = view_extent(qside[i], a->B, a->n_q, a->H, a->q_stride_b, a->q_stride_n,
+                         a->q_stride_h, a->D, es);
+      t[4 + i] = view_extent(kside[i], a->B, a->n_k, a->H, a->k_stride_b, a->k_stride_n,
+                             a->k_stride_h, a->D, es);
     }
+    t[8] = range_extent(a->lse, lse_bytes);
+    t[9] = range_extent(tangent ? a->d_lse : nullptr, lse_bytes);
+    const Extent w = range_extent(workspace, need);
+    for (const Extent &x : t)
+      if (extents_overlap(w, x)) return ATTN_JVP_ERR_UNSUPPORTED;
   }
   int device = -1;
   if (hipGetDevice(&device) != hipSuccess) return ATTN_JVP_ERR_HIP;
@@ -482,12 +642,24 @@ extern "C" int attn_jvp_bwd(const attn_jvp_bwd_args *a, const attn_jvp_mask *m, 
     if (!aligned16(p)) return ATTN_JVP_ERR_ALIGN;
   for (const void *p : outs)
     if (!aligned16(p)) return ATTN_JVP_ERR_ALIGN;
-  for (const void *p : ins)
-    for (const void *o : outs)
-      if (p == o) return ATTN_JVP_ERR_UNSUPPORTED;
-  for (int i = 0; i < 4; ++i)
-    for (int j = i + 1; j < 4; ++j)
-      if (outs[i] == outs[j]) return ATTN_JVP_ERR_UNSUPPORTED;
+  {
+    // no output may share a byte with an input or another output
+    const int64_t rows_bytes = int64_t(a->B) * a->H * a->n_q * 4;
+    const Extent in_ext[6] = {
+        view_extent(a->q, a->B, a->n_q, a->H, qs[0], qs[1], qs[2], a->D, es),
+        view_extent(a->o, a->B, a->n_q, a->H, qs[0], qs[1], qs[2], a->D, es),
+        view_extent(a->g_o, a->B, a->n_q, a->H, qs[0], qs[1], qs[2], a->D, es),
+        view_extent(a->k, a->B, a->n_k, a->H, ks[0], ks[1], ks[2], a->D, es),
+        view_extent(a->v, a->B, a->n_k, a->H, ks[0], ks[1], ks[2], a->D, es),
+        range_extent(a->lse, rows_bytes)};
+    const Extent out_ext[4] = {
+        view_extent(a->g_q, a->B, a->n_q, a->H, qs[0], qs[1], qs[2], a->D, es),
+        view_extent(a->g_k, a->B, a->n_k, a->H, ks[0], ks[1], ks[2], a->D, es),
+        view_extent(a->g_v, a->B, a->n_k, a->H, ks[0], ks[1], ks[2], a->D, es),
+        range_extent(a->delta, rows_bytes)};
+    const int st = check_disjoint(in_ext, 6, out_ext, 4);
+    if (st != ATTN_JVP_OK) return st;
+  }
 
   int device = -1;
   if (hipGetDevice(&device) != hipSuccess) return ATTN_JVP_ERR_HIP;

@@ -228,6 +228,33 @@ int transpose_mask(const attn_jvp_mask *m, attn_jvp_mask **out) {
   return ATTN_JVP_OK;
 }
 
+// Number of (query tile, key block) entries of the schedule, counted without
+// building it: per tile, the union of the key-block intervals that the ranges
+// of its groups touch.  Exact, in 64 bits.
+static int64_t count_entries(const attn_jvp_mask *m, int BM, int BN) {
+  const int n_tiles = (m->n_q + BM - 1) / BM;
+  const int n_groups = int(m->group_q_begin.size()) - 1;
+  std::vector<std::pair<int64_t, int64_t>> iv;
+  int64_t total = 0;
+  int g0 = 0;
+  for (int t = 0; t < n_tiles; ++t) {
+    const int r0 = t * BM, r1 = std::min(m->n_q, r0 + BM);
+    while (g0 + 1 < n_groups && m->group_q_begin[g0 + 1] <= r0) ++g0;
+    iv.clear();
+    for (int g = g0; g < n_groups && m->group_q_begin[g] < r1; ++g)
+      for (int r = m->range_ptr[g]; r < m->range_ptr[g + 1]; ++r)
+        iv.push_back({m->k_begin[r] / BN, (int64_t(m->k_end[r]) + BN - 1) / BN});
+    std::sort(iv.begin(), iv.end());
+    int64_t hi = -1;
+    for (auto &x : iv) {
+      const int64_t lo = std::max(x.first, hi);
+      if (x.second > lo) total += x.second - lo;
+      hi = std::max(hi, x.second);
+    }
+  }
+  return total;
+}
+
 // Classify every key block for every query tile.  A block is listed when some
 // row of the tile admits some key of it; it is full when every existing row
 // of the tile admits all block_n keys (so a block reaching past n_k is never
@@ -331,6 +358,11 @@ const HostSchedule *host_schedule_locked(const attn_jvp_mask *m, int block_m, in
   if (it != m->host_sched.end()) {
     *status = ATTN_JVP_OK;
     return &it->second;
+  }
+  // entry and partial-block indices are 32-bit on the device
+  if (count_entries(m, block_m, block_n) > int64_t(kMaxScheduleEntries)) {
+    *status = ATTN_JVP_ERR_SHAPE;
+    return nullptr;
   }
   try {
     HostSchedule s;

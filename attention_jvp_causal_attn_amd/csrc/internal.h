@@ -231,5 +231,8 @@ constexpr int kBwdBlockMWide = 256;   // backward: 8 waves x 32 rows (or keys)
 constexpr int kBwdBlockN = 32;        // backward: blocks of 32 keys (or queries)
 constexpr int kF32BlockM = 64;
 constexpr int kF32BlockN = 32;
+// Largest schedule (query tile, key block entries) of one tile shape: entry
+// offsets and partial-block indices are int32 on the device.
+constexpr int32_t kMaxScheduleEntries = 0x7fffffff;
 
 }  // namespace attnjvp

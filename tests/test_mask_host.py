@@ -214,6 +214,11 @@ def test_mask_errors():
         with pytest.raises(E) as ei:
             aj.attn_jvp_mask_rects(**args)
         assert ei.value.status == aj._lib.ATTN_JVP_ERR_MASK, b
+    # CSR pointers past the end of the key arrays are refused before the C
+    # builder could read beyond them
+    for rp in ([0, 1, 5], [0, 3, 3], [0, -1, 2]):
+        with pytest.raises(ValueError):
+            aj.attn_jvp_mask_rects(10, 8, [0, 4, 10], rp, [0, 2], [3, 8])
     with pytest.raises(E) as ei:
         aj.attn_jvp_mask_rects(0, 8, [0], [0], [], [])
     assert ei.value.status == aj._lib.ATTN_JVP_ERR_SHAPE
@@ -368,3 +373,24 @@ def test_split_errors():
     for args in [(128, 32, 0), (128, 32, -3), (128, 48, 2), (0, 32, 2)]:
         with pytest.raises(aj.AttnJvpError):
             aj.attn_jvp_mask_split_schedule(m, *args)
+
+
+def test_schedule_larger_than_int32_entries_is_refused():
+    # The device schedule indexes its (tile, key block) entries with int32: a
+    # dense 2^26 x 2^26 mask would need 2^18 tiles x 2^21 blocks = 2^39
+    # entries at 256 x 32 tiles.  The entries are counted (not built) first
+    # and the schedule is refused with ERR_SHAPE, without allocating it.
+    n = 1 << 26
+    m = aj.attn_jvp_mask_dense(n, n)
+    with pytest.raises(aj.AttnJvpError) as ei:
+        aj.attn_jvp_mask_schedule(m, 256, 32)
+    assert ei.value.status == aj._lib.ATTN_JVP_ERR_SHAPE
+    with pytest.raises(aj.AttnJvpError) as ei:
+        aj.attn_jvp_mask_split_schedule(m, 256, 32, 2)
+    assert ei.value.status == aj._lib.ATTN_JVP_ERR_SHAPE
+    # 2^31 - 1 entries is the largest schedule: 46,341 tiles of one row x
+    # 46,341 blocks of 32 keys is 2,147,488,281 > 2^31 - 1 ...
+    big = aj.attn_jvp_mask_dense(46341, 46341 * 32)
+    with pytest.raises(aj.AttnJvpError) as ei:
+        aj.attn_jvp_mask_schedule(big, 1, 32)
+    assert ei.value.status == aj._lib.ATTN_JVP_ERR_SHAPE
