@@ -248,3 +248,41 @@ def test_long_lists_cross_entry_refills_bwd(n_q, n_k, D):
     x = {"q": xq["q"], "k": xk["k"], "v": xk["v"]}
     g = xq["dq"]
     parity(x, g, pred, aj.attn_jvp_mask_dense(n_q, n_k))
+
+
+def test_chunkwise_65k_bwd_every_tile():
+    # The backward at the benchmarked shape (chunk-wise 65,520 tokens, B=1,
+    # H=12, D=128), NaN-filled outputs: every element of every slice written
+    # and finite.  Slice h=4 against the oracle: dQ and D on the first and
+    # last row of every 256-row query tile and of every chunk, dK and dV on
+    # the first and last key of every 256-key tile and of every chunk.
+    w = WORKLOADS[3]
+    say(f"case: bwd {w.describe()}")
+    x = make_inputs(w)
+    g = make_random(w.B, w.N, w.H, w.D, dtype=w.dtype, seed=9960)["q"]
+    mask = aj.attn_jvp_mask_tf(w.n_frames, w.tokens_per_frame, w.frames_per_chunk)
+    xd = {k: v.cuda() for k, v in x.items()}
+    gd = g.cuda()
+    o, _, lse = aj.attn_jvp_fwd(xd["q"], xd["k"], xd["v"], None, None, None, mask)
+    gq, gk, gv = (torch.full_like(xd["q"], float("nan")) for _ in range(3))
+    delta = torch.full_like(lse, float("nan"))
+    aj.attn_jvp_bwd(xd["q"], xd["k"], xd["v"], o, gd, lse, mask, g_q=gq, g_k=gk, g_v=gv,
+                    delta=delta)
+    torch.cuda.synchronize()
+    for name, t in (("dQ", gq), ("dK", gk), ("dV", gv), ("D", delta)):
+        assert bool(torch.isfinite(t).all()), f"{name}: an element is unwritten or not finite"
+    pred = tf_allowed(w.n_frames, w.tokens_per_frame, w.frames_per_chunk)
+    C, Nc = w.unit_tokens, w.n_frames * w.tokens_per_frame
+    edges = {s + u * C + o_ for s in (0, Nc) for u in range(w.n_units) for o_ in (0, C - 1)}
+    edges |= {t0 + o_ for t0 in range(0, w.N, 256) for o_ in (0, 255) if t0 + o_ < w.N}
+    idx = np.array(sorted(edges))
+    h = 4
+    say(f"  every element written and finite; {len(idx)} rows and keys of slice h={h} "
+        "against the oracle")
+    sl = {k: v[:, :, h:h + 1] for k, v in x.items()}
+    dQ, dK, dV, Ds = masked_attention_grad(sl["q"], sl["k"], sl["v"], g[:, :, h:h + 1], pred,
+                                           rows=idx, keys=idx)
+    check("dQ", f64(gq[:, idx, h:h + 1]), dQ)
+    check("dK", f64(gk[:, idx, h:h + 1]), dK)
+    check("dV", f64(gv[:, idx, h:h + 1]), dV)
+    check("D", f64(delta[:, h:h + 1, idx]), Ds)

@@ -219,15 +219,24 @@ def test_head_and_batch_permutation_is_bitwise():
     assert torch.equal(a[2][:, perm_h].flip(0), b[2])
 
 
-def test_tangent_linearity():
-    _, mask, x = _tf_case("bf16", seed=9900)
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_tangent_linearity(dtype):
+    # Doubling every tangent doubles every value the tangent path forms (the
+    # products, exponent sums, the bf16 roundings of P*dS, mu and T), exactly,
+    # in binary floating point away from overflow and subnormals: dO and the
+    # LSE tangent double bit for bit and O, LSE do not change.
+    _, mask, x = _tf_case(dtype, seed=9900)
     xd = to_dev(x)
-    _, d1, _ = run(xd, mask)
-    y = dict(xd)
-    for n in ("dq", "dk", "dv"):
-        y[n] = (xd[n].float() * 2.0).to(xd[n].dtype)   # exact in bf16
-    _, d2, _ = run(y, mask)
-    check("dO(2t) vs 2 dO(t)", f64(d2), 2.0 * f64(d1), 1e-2)
+    o1, d1, l1, g1 = aj.attn_jvp_fwd(xd["q"], xd["k"], xd["v"], xd["dq"], xd["dk"], xd["dv"],
+                                     mask, lse_tangent=True)
+    y = {n: xd[n] * 2 for n in ("dq", "dk", "dv")}
+    assert all(torch.equal(y[n] / 2, xd[n]) for n in y)      # exact scaling of the inputs
+    o2, d2, l2, g2 = aj.attn_jvp_fwd(xd["q"], xd["k"], xd["v"], y["dq"], y["dk"], y["dv"], mask,
+                                     lse_tangent=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert torch.equal(d2, d1 * 2), "dO(2t) differs from 2 dO(t)"
+    assert torch.equal(g2, g1 * 2), "dLSE(2t) differs from 2 dLSE(t)"
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -297,6 +306,8 @@ WORK_MAP_CASES = [
     (2, 5, 1024),  # 10 slices: groups of 4 XCDs, 5 slices per group
     (1, 2, 2048),  # groups of 4 XCDs, 2 tile slots each
     (4, 2, 400),   # 8 slices: one slice group per XCD
+    (1, 12, 512),  # 12 slices, 2 tiles: groups of 2 XCDs (the 65,520-token workloads' map)
+    (1, 4, 512),   # 4 slices, 2 tiles: groups of 2 XCDs, one slice per group
 ]
 
 
@@ -381,30 +392,75 @@ def test_strided_views_of_fused_buffers():
 
 # ------------------------------------------- full-size workloads, sampled ----
 
+BF16_TILE = 256   # query rows per workgroup of both bf16 head dims
+
+
 def sample_rows(w, n_random=48, seed=0):
-    """Unit-boundary rows of both streams, query-tile boundary rows, and random
-    rows."""
+    """The first and last row of every 256-row query tile, the first and last
+    row of every unit of both streams, and random rows."""
     Nc, C = w.n_frames * w.tokens_per_frame, w.unit_tokens
     rows = set()
     for s in (0, Nc):
         for u in range(w.n_units):
             rows.update({s + u * C, s + u * C + C - 1})
-    rows.update({0, w.N - 1, 127, 128, 8191, 8192})
+    for t0 in range(0, w.N, BF16_TILE):
+        rows.update({t0, min(w.N, t0 + BF16_TILE) - 1})
+    rows.update({0, w.N - 1})
     rng = np.random.default_rng(seed)
     rows.update(rng.integers(0, w.N, size=n_random).tolist())
     return np.array(sorted(r for r in rows if 0 <= r < w.N))
 
 
 @pytest.mark.parametrize("wid", [2, 3, 4, 5])
-def test_full_size_workload_sampled(wid):
+def test_full_size_workload_every_tile(wid):
+    # Every (b, h) slice of the full workload in the launch the benchmark
+    # times, outputs NaN-filled beforehand: every element written and finite;
+    # the first and last row of every query tile, every unit boundary and
+    # random rows compared with the oracle element by element.
     w = WORKLOADS[wid]
     say(f"case: workload {wid}: {w.describe()}")
     x = make_inputs(w)
+    xd = to_dev(x)
     mask = aj.attn_jvp_mask_tf(w.n_frames, w.tokens_per_frame, w.frames_per_chunk)
     pred = tf_allowed(w.n_frames, w.tokens_per_frame, w.frames_per_chunk)
+    o = torch.full_like(xd["q"], float("nan"))
+    do = torch.full_like(xd["q"], float("nan"))
+    lse = torch.full((w.B, w.H, w.N), float("nan"), dtype=torch.float32, device=DEV)
+    aj.attn_jvp_fwd(xd["q"], xd["k"], xd["v"], xd["dq"], xd["dk"], xd["dv"], mask, o=o, d_o=do,
+                    lse=lse)
+    torch.cuda.synchronize()
+    for name, t in (("O", o), ("dO", do), ("LSE", lse)):
+        assert bool(torch.isfinite(t).all()), f"{name}: an element is unwritten or not finite"
     rows = sample_rows(w, seed=wid)
-    say(f"  {len(rows)} sampled rows per (b, h)")
-    parity(x, pred, mask, TOL[torch.bfloat16], rows=rows)
+    say(f"  every element written and finite; {len(rows)} rows per (b, h) against the oracle "
+        f"({w.B * w.H} slices)")
+    O, dO, LSE = masked_attention_jvp(x["q"], x["k"], x["v"], x["dq"], x["dk"], x["dv"], pred,
+                                      rows=rows)
+    sel = torch.as_tensor(rows)
+    tol = TOL[torch.bfloat16]
+    check("O", f64(o[:, sel]), O, tol)
+    check("dO", f64(do[:, sel]), dO, tol)
+    check("LSE", f64(lse[:, :, sel]), LSE, tol)
+
+
+def test_chunkwise_65k_one_full_slice():
+    # one whole (b, h) slice of the chunk-wise 65,520-token workload, every
+    # row, compared with the oracle element by element
+    w = WORKLOADS[3]
+    h = 7
+    say(f"case: workload 3, every row of slice (b=0, h={h}): {w.describe()}")
+    x = make_inputs(w)
+    xd = to_dev(x)
+    mask = aj.attn_jvp_mask_tf(w.n_frames, w.tokens_per_frame, w.frames_per_chunk)
+    pred = tf_allowed(w.n_frames, w.tokens_per_frame, w.frames_per_chunk)
+    o, do, lse = run(xd, mask)
+    sl = {k: v[:, :, h:h + 1] for k, v in x.items()}
+    O, dO, LSE = masked_attention_jvp(sl["q"], sl["k"], sl["v"], sl["dq"], sl["dk"], sl["dv"],
+                                      pred)
+    tol = TOL[torch.bfloat16]
+    check("O", f64(o[:, :, h:h + 1]), O, tol)
+    check("dO", f64(do[:, :, h:h + 1]), dO, tol)
+    check("LSE", f64(lse[:, h:h + 1]), LSE, tol)
 
 
 def test_head_dim_64_long_sequence_sampled():

@@ -200,6 +200,8 @@ def test_full_size_chunkwise_split_sampled():
     rng = np.random.default_rng(3)
     Nc, C = w.n_frames * w.tokens_per_frame, w.unit_tokens
     rows = {0, w.N - 1, Nc - 1, Nc, Nc + C, 2 * C - 1}
+    # the first and last row of every 256-row query tile (cut or whole)
+    rows.update(r for t0 in range(0, w.N, 256) for r in (t0, min(w.N, t0 + 256) - 1))
     rows.update(rng.integers(0, w.N, size=40).tolist())
     rows = np.array(sorted(rows))
     parity(x, pred, mask, 2, "bf16", rows=rows)
