@@ -9,7 +9,11 @@ of 3 frames, N = 65,520), bf16.
 Prints one JSON line on stdout; progress goes to stderr.
 
   python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload 3]
-                  [--no-cpu-baseline] [--copy-calibration]
+                  [--no-cpu-baseline] [--no-configs] [--copy-calibration]
+
+Besides the headline workload, the line carries ``configs``: the JVP and the
+primal-only kernel (tangents compiled out) on the other bf16 workloads, and
+the latency of the tiny fp32 workload (median of 200 single calls).
 """
 
 import argparse
@@ -134,41 +138,117 @@ def clock_under_load(fn, n_calls=60):
     return out
 
 
-def cpu_baseline(w, x, target_s=18.0):
-    """The fp64 oracle on a bounded sample of the same workload: query rows of
-    slice (b=0, h=0) spread over every unit of both streams, sized to about
-    ``target_s`` seconds of host time; scaled to TFLOP/s with the same
-    12*D-per-admissible-pair count as the GPU figure."""
-    import numpy as np
-    from oracle import masked_attention_jvp, tf_allowed
+def blas_info():
+    """(library name, thread count) of the BLAS numpy calls, if threadpoolctl
+    can tell."""
     try:
         from threadpoolctl import threadpool_info
-        threads = max([t.get("num_threads", 1) for t in threadpool_info()
-                       if t.get("user_api") == "blas"] or [1])
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
+        blas = [t for t in threadpool_info() if t.get("user_api") == "blas"]
+        if blas:
+            return blas[0].get("internal_api", "unknown"), int(blas[0].get("num_threads", 1))
+    except Exception:  # noqa: BLE001 - report what is known
+        pass
+    return "unknown", None
+
+
+def cpu_baseline(w, x, h=0):
+    """The fp64 oracle (as it stands, untuned) on one complete (b, h) slice of
+    the workload: every query row.  Every slice of a workload holds the same
+    admissible pairs, so the whole call takes B * H times as long; the rate is
+    scaled with the same 12 * D FLOP per admissible pair as the GPU figure."""
+    from oracle import masked_attention_jvp, tf_allowed
     pred = tf_allowed(w.n_frames, w.tokens_per_frame, w.frames_per_chunk)
-    sl = {k: v[:1, :, :1] for k, v in x.items()}          # slice (b=0, h=0)
-    rng = np.random.default_rng(12345)
+    sl = {k: v[:1, :, h:h + 1] for k, v in x.items()}    # slice (b=0, h)
+    pairs = visible_pairs(w)
+    t0 = time.perf_counter()
+    masked_attention_jvp(sl["q"], sl["k"], sl["v"], sl["dq"], sl["dk"], sl["dv"], pred)
+    dt = time.perf_counter() - t0
+    lib, threads = blas_info()
+    cores = len(os.sched_getaffinity(0))
+    return {"value": 12 * w.D * pairs / dt / 1e12, "unit": "TFLOP/s", "cores": cores,
+            "kind": "oracle",
+            "sample": (f"fp64 numpy oracle on one complete (b,h) slice of {w.name} "
+                       f"({w.N} query rows, {pairs} admissible pairs) in {dt:.1f} s; the "
+                       f"whole call is B*H = {w.B * w.H} such slices ({w.B * w.H * dt:.0f} s)"),
+            "slice_s": round(dt, 2), "call_s_scaled": round(w.B * w.H * dt, 1),
+            "blas": {"library": lib, "threads": threads}, "host_cpus_in_affinity": cores}
 
-    def run(n_rows):
-        rows = np.sort(rng.choice(w.N, size=n_rows, replace=False))
-        pairs = int(pred(rows).sum())
-        t0 = time.perf_counter()
-        masked_attention_jvp(sl["q"], sl["k"], sl["v"], sl["dq"], sl["dk"], sl["dv"], pred,
-                             rows=rows)
-        return time.perf_counter() - t0, pairs, n_rows
 
-    dt, pairs, n = run(128)
-    for _ in range(3):  # grow the sample until it takes 10-30 s of host time
-        if dt >= 10.0 or n >= w.N:
-            break
-        n = int(min(w.N, max(n + 1, n * target_s / max(dt, 1e-3))))
-        dt, pairs, n = run(n)
-    tflops = 12 * w.D * pairs / dt / 1e12
-    return {"value": tflops, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": (f"fp64 numpy oracle on {n} random query rows of one (b,h) slice "
-                       f"({pairs} admissible pairs, {dt:.1f} s), scaled by 12*D FLOP per pair")}
+def bench_workload(wid, args, stream):
+    """JVP and primal-only kernels on workload ``wid`` (bf16), timed like the
+    headline: algorithmic TFLOP/s and the JVP/primal time ratio."""
+    import torch
+    import attention_jvp_causal_attn_amd as aj
+    from attention_jvp_causal_attn_amd.inputs import WORKLOADS, make_inputs
+    w = WORKLOADS[wid]
+    log(f"config {wid}: {w.describe()}")
+    xd = {k: v.to("cuda") for k, v in make_inputs(w).items()}
+    mask = aj.attn_jvp_mask_tf(w.n_frames, w.tokens_per_frame, w.frames_per_chunk)
+    pairs = mask.info()["n_visible_pairs"]
+    assert pairs == visible_pairs(w)
+    o, do = torch.empty_like(xd["q"]), torch.empty_like(xd["q"])
+    lse = torch.empty(w.B, w.H, w.N, dtype=torch.float32, device="cuda")
+
+    def jvp():
+        aj.attn_jvp_fwd(xd["q"], xd["k"], xd["v"], xd["dq"], xd["dk"], xd["dv"], mask,
+                        o=o, d_o=do, lse=lse, stream=stream)
+
+    def primal():
+        aj.attn_jvp_fwd(xd["q"], xd["k"], xd["v"], None, None, None, mask, o=o, lse=lse,
+                        stream=stream)
+
+    flops = 12 * w.D * pairs * w.B * w.H
+    ms, _ = time_calls(jvp, args.steps, args.warmup, stream)
+    pms, _ = time_calls(primal, args.steps, args.warmup, stream)
+    tf, ptf = flops / ms / 1e9, flops / 3 / pms / 1e9
+    log(f"  JVP {ms:.3f} ms ({tf:.1f} TFLOP/s, {100 * tf / PEAK_BF16_TFLOPS:.1f} %), primal "
+        f"{pms:.3f} ms ({ptf:.1f} TFLOP/s), JVP/primal {ms / pms:.2f}")
+    out = {"workload": w.name, "B": w.B, "H": w.H, "D": w.D, "N": w.N,
+           "visible_pairs_per_slice": pairs,
+           "jvp": {"ms": round(ms, 4), "tflops": round(tf, 2),
+                   "pct_of_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2)},
+           "primal_only": {"ms": round(pms, 4), "tflops": round(ptf, 2),
+                           "pct_of_bf16_peak": round(100 * ptf / PEAK_BF16_TFLOPS, 2)},
+           "jvp_over_primal_time": round(ms / pms, 3)}
+    del xd, o, do, lse
+    mask.free()
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_tiny_latency(stream, calls=200):
+    """Latency of the tiny fp32 workload (B=1, H=2, D=64, 128 tokens): each of
+    ``calls`` JVP calls timed alone with events, after warm-up; the median."""
+    import torch
+    import attention_jvp_causal_attn_amd as aj
+    from attention_jvp_causal_attn_amd.inputs import WORKLOADS, make_inputs
+    w = WORKLOADS[1]
+    xd = {k: v.to("cuda") for k, v in make_inputs(w).items()}
+    mask = aj.attn_jvp_mask_tf(w.n_frames, w.tokens_per_frame, w.frames_per_chunk)
+    o, do = torch.empty_like(xd["q"]), torch.empty_like(xd["q"])
+    lse = torch.empty(w.B, w.H, w.N, dtype=torch.float32, device="cuda")
+
+    def jvp():
+        aj.attn_jvp_fwd(xd["q"], xd["k"], xd["v"], xd["dq"], xd["dk"], xd["dv"], mask,
+                        o=o, d_o=do, lse=lse, stream=stream)
+
+    for _ in range(20):
+        jvp()
+    torch.cuda.synchronize()
+    per = []
+    for _ in range(calls):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        jvp()
+        e1.record(stream)
+        e1.synchronize()
+        per.append(1e3 * e0.elapsed_time(e1))
+    per.sort()
+    log(f"config 1 ({w.name}): median latency {per[len(per) // 2]:.1f} us over {calls} calls")
+    return {"workload": w.name, "B": w.B, "H": w.H, "D": w.D, "N": w.N, "dtype": w.dtype,
+            "calls": calls, "latency_us_median": round(per[len(per) // 2], 2),
+            "latency_us_p10": round(per[len(per) // 10], 2),
+            "latency_us_p90": round(per[(9 * len(per)) // 10], 2)}
 
 
 def bench_split(w, args, stream):
@@ -216,6 +296,10 @@ def main():
     ap.add_argument("--no-primal", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-split", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other workloads (configs object)")
+    ap.add_argument("--no-clocks", action="store_true",
+                    help="skip sampling the GPU clocks under load")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter scaling)")
     args = ap.parse_args()
@@ -268,7 +352,7 @@ def main():
     value = flops / (ms * 1e-3) / 1e12
     log(f"JVP: {ms:.3f} ms/call, {value:.1f} TFLOP/s "
         f"({100 * value / PEAK_BF16_TFLOPS:.1f}% of bf16 peak)")
-    clocks = clock_under_load(jvp)
+    clocks = None if args.no_clocks else clock_under_load(jvp)
     log(f"clocks under load: {clocks}")
     res = {
         "metric": "attention-JVP TFLOP/s (primal+tangent) and % of bf16 MFMA peak, 1 GPU",
@@ -318,12 +402,20 @@ def main():
                            "flop_per_pair": 10 * w.D}
     if not args.no_split:
         res["kv_cache_last_frame"] = bench_split(w, args, stream)
+    if not args.no_configs:
+        del xd, o, do, lse
+        torch.cuda.empty_cache()
+        configs = {"1": bench_tiny_latency(stream)}
+        for wid in (2, 3, 4, 5):
+            if wid != args.workload:
+                configs[str(wid)] = bench_workload(wid, args, stream)
+        res["configs"] = configs
     traffic = measured_traffic(w.name)
     res["roofline"] = {"bound": "mfma", "achieved": round(value, 2), "peak": PEAK_BF16_TFLOPS,
                        "unit": "TFLOP/s", "frac": round(value / PEAK_BF16_TFLOPS, 4),
                        "traffic": traffic}
     if not args.no_cpu_baseline:
-        log("timing the fp64 CPU oracle on a sample ...")
+        log("timing the fp64 CPU oracle on one complete (b, h) slice ...")
         res["cpu_baseline"] = cpu_baseline(w, x)
         log(f"cpu baseline: {res['cpu_baseline']}")
     print(json.dumps(res), flush=True)
