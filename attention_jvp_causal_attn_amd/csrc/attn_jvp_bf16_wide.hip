@@ -66,7 +66,7 @@ constexpr int kThreads = 512;
 constexpr int kWaves = 8;
 constexpr int BM = kBf16BlockMWide;  // 256 query rows per workgroup
 constexpr int BN = kBf16BlockN;      // 32 keys per block
-constexpr int kStages = 2;
+constexpr int kStages = 2;           // block j + 1 is copied while block j is computed
 static_assert(BM == 32 * kWaves && BN == 32, "one wave per 32 rows, 32-key blocks");
 
 constexpr float kNegInf = -__builtin_inff();
@@ -84,7 +84,7 @@ struct Geo {
   static constexpr int TILE = BN * KCH;  // chunks of one 32-row tile
 };
 
-template <int D>
+template <int D, bool TAN>
 struct alignas(16) StageTile {
   uint4 k[Geo<D>::TILE];
   uint4 dk[Geo<D>::TILE];
@@ -92,6 +92,22 @@ struct alignas(16) StageTile {
   uint4 dv[Geo<D>::TILE];
   uint32_t bits[BM];
 };
+template <int D>
+struct alignas(16) StageTile<D, false> {  // primal: no tangent tiles
+  uint4 k[Geo<D>::TILE];
+  uint4 v[Geo<D>::TILE];
+  uint32_t bits[BM];
+};
+// LDS byte offset of tensor t (0 K, 1 V, 2 dK, 3 dV) inside a stage.
+template <int D, bool TAN>
+constexpr uint32_t tile_offset(int t) {
+  using ST = StageTile<D, TAN>;
+  if constexpr (TAN)
+    return uint32_t(t == 0 ? offsetof(ST, k) : t == 1 ? offsetof(ST, v)
+                    : t == 2 ? offsetof(ST, dk) : offsetof(ST, dv));
+  else
+    return uint32_t(t == 0 ? offsetof(ST, k) : offsetof(ST, v));
+}
 
 // Position of K row m of the 32x32 score tile: bits 2 and 3 swapped.  The
 // MFMA output element (row 8j + 4h + i) then holds key 16(j/2) + 8h + 4(j%2) + i,
@@ -180,7 +196,7 @@ __device__ __forceinline__ void issue_block(uint32_t st, int wave, const KernelP
                                             const __bf16 *kb_, const __bf16 *dkb_,
                                             const __bf16 *vb_, const __bf16 *dvb_, int key0,
                                             const uint32_t *bits_src) {
-  using ST = StageTile<D>;
+  using ST = StageTile<D, TAN>;
   constexpr int TILE = Geo<D>::TILE;
   constexpr int COPIES = (TAN ? 4 : 2) * TILE / kThreads;
   const int lane = threadIdx.x & 63;
@@ -193,16 +209,16 @@ __device__ __forceinline__ void issue_block(uint32_t st, int wave, const KernelP
     // serves the four tensors (the general loop below compiles slower here)
     const DmaOffsets o = dma_offsets<D>(int(threadIdx.x), p.k_sn, rows_valid);
     const uint32_t chunk = uint32_t(wave * 64) * 16u;
-    dma16(kb_ + boff, o.k, st + uint32_t(offsetof(ST, k)) + chunk);
-    dma16(vb_ + boff, o.v, st + uint32_t(offsetof(ST, v)) + chunk);
-    if (TAN) {
+    dma16(kb_ + boff, o.k, st + tile_offset<D, TAN>(0) + chunk);
+    dma16(vb_ + boff, o.v, st + tile_offset<D, TAN>(1) + chunk);
+    if constexpr (TAN) {
       // an absent tangent tensor is zero: copy the zero row into every row
       const DmaOffsets oz = dma_offsets<D>(int(threadIdx.x), 0, 1);
       const bool zk = dkb_ == nullptr, zv = dvb_ == nullptr;
       dma16(zk ? static_cast<const void *>(kZeroRow) : dkb_ + boff, zk ? oz.k : o.k,
-            st + uint32_t(offsetof(ST, dk)) + chunk);
+            st + tile_offset<D, TAN>(2) + chunk);
       dma16(zv ? static_cast<const void *>(kZeroRow) : dvb_ + boff, zv ? oz.v : o.v,
-            st + uint32_t(offsetof(ST, dv)) + chunk);
+            st + tile_offset<D, TAN>(3) + chunk);
     }
   } else {
 #pragma unroll
@@ -210,9 +226,7 @@ __device__ __forceinline__ void issue_block(uint32_t st, int wave, const KernelP
       const int c0 = i * kThreads + wave * 64;  // wave-uniform
       const int t = c0 / TILE;                  // 0 K, 1 V, 2 dK, 3 dV
       const int c = c0 % TILE + lane;
-      const uint32_t dst = st + uint32_t(c0 % TILE) * 16u +
-                           uint32_t(t == 0 ? offsetof(ST, k) : t == 1 ? offsetof(ST, v)
-                                    : t == 2 ? offsetof(ST, dk) : offsetof(ST, dv));
+      const uint32_t dst = st + uint32_t(c0 % TILE) * 16u + tile_offset<D, TAN>(t);
       // an absent tangent tensor is zero: copy the zero row into every row
       const __bf16 *src = t == 0 ? kb_ : t == 1 ? vb_ : t == 2 ? dkb_ : dvb_;
       if (src == nullptr) {
@@ -227,7 +241,7 @@ __device__ __forceinline__ void issue_block(uint32_t st, int wave, const KernelP
   // mask bits: BM words = 64 chunks; wave w copies chunks 8w .. 8w+7 (lanes 0..7)
   if (lane < 8)
     dma16(bits_src, uint32_t(wave * 8 + lane) * 16u,
-          st + uint32_t(offsetof(StageTile<D>, bits)) + uint32_t(wave) * 128u);
+          st + uint32_t(offsetof(ST, bits)) + uint32_t(wave) * 128u);
 }
 
 // Key-loop code shape: every kernel holds its per-lane LDS read offsets
@@ -252,9 +266,19 @@ __device__ __forceinline__ bf16x8 row_read(const uint4 *row, int t, int hh, int 
     return as_bf16x8(row[(2 * t + hh) ^ x]);
 }
 
+// The tangent tiles of a stage (JVP kernels only).
+template <int D, bool TAN>
+__device__ __forceinline__ const uint4 *dk_tile(const StageTile<D, TAN> *st) {
+  if constexpr (TAN) return st->dk; else return nullptr;
+}
+template <int D, bool TAN>
+__device__ __forceinline__ const uint4 *dv_tile(const StageTile<D, TAN> *st) {
+  if constexpr (TAN) return st->dv; else return nullptr;
+}
+
 // S^T = K Q^T and dS^T = K dQ^T + dK Q^T; Q from registers, dQ from LDS.
 template <int D, bool TAN>
-__device__ __forceinline__ void score_block(const StageTile<D> *st, const uint4 *dq_lds,
+__device__ __forceinline__ void score_block(const StageTile<D, TAN> *st, const uint4 *dq_lds,
                                             const bf16x8 *qf, int row_in_tile, f32x16 &S,
                                             f32x16 &dS) {
   const int lane = threadIdx.x & 63;
@@ -262,7 +286,7 @@ __device__ __forceinline__ void score_block(const StageTile<D> *st, const uint4 
   const int krow = swap_bits23(col);
   constexpr int KCH = Geo<D>::KCH, KSTEPS = Geo<D>::KSTEPS;
   const uint4 *Ks = st->k + krow * KCH;
-  const uint4 *dKs = st->dk + krow * KCH;
+  const uint4 *dKs = dk_tile(st) + krow * KCH;
   const uint4 *dQs = dq_lds + row_in_tile * KCH;
   constexpr bool kXad = kXadReads<D, TAN>;
   const int kx = k_swz<D>(krow), qx = k_swz<D>(row_in_tile);
@@ -286,20 +310,22 @@ __device__ __forceinline__ void score_block(const StageTile<D> *st, const uint4 
   }
 }
 
-// Masking, online-softmax update and value step of one key block.
+// Masking and online-softmax update of one key block: the block's weights P
+// (and P * dS) rounded to bf16 for the value MFMAs, l and mu updated, the
+// accumulators rescaled when the reference max moves.
 template <int D, bool TAN>
-__device__ __forceinline__ void softmax_value_block(const StageTile<D> *st, f32x16 S, f32x16 dS,
-                                                    f32x16 *accO, f32x16 *accT, float &m_ref,
-                                                    float &l_run, float &mu_run, bool partial,
-                                                    int row_in_tile, float scale_log2,
-                                                    float scale) {
-  constexpr int KCH = Geo<D>::KCH, DT = Geo<D>::DT;
+__device__ __forceinline__ void softmax_block(const uint32_t *bits_row, f32x16 S, f32x16 dS,
+                                              f32x16 *accO, f32x16 *accT, float &m_ref,
+                                              float &l_run, float &mu_run, bool partial,
+                                              float scale_log2, float scale, bf16x8 *pb,
+                                              bf16x8 *pdsb) {
+  constexpr int DT = Geo<D>::DT;
   const int lane = threadIdx.x & 63;
   const int hh = lane >> 5;
   if (partial) {
     // this lane-half's keys 8hh + {0..7, 16..23}, so the bit positions below
     // are constants
-    const uint32_t bits = st->bits[row_in_tile] >> (8 * hh);
+    const uint32_t bits = *bits_row >> (8 * hh);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int j = r >> 2, i = r & 3;
@@ -329,7 +355,6 @@ __device__ __forceinline__ void softmax_value_block(const StageTile<D> *st, f32x
   }
   const float m_use = m_ref == kNegInf ? 0.f : m_ref;
   float pr[16], pds[16];
-  bf16x8 pb[2], pdsb[2];
   // l and mu are summed from the bf16 weights the value MFMAs consume, two
   // per v_dot2 (half the vector instructions of fp32 sums, and O, dO are then
   // normalised by exactly the weights they were accumulated with)
@@ -360,6 +385,17 @@ __device__ __forceinline__ void softmax_value_block(const StageTile<D> *st, f32x
   }
   l_run += lsum;
   if (TAN) mu_run += musum;
+}
+
+// Value step of one key block: A^T += V^T P^T, and with tangents
+// T^T += V^T (P*dS)^T + dV^T P^T, V and dV read transposed from the stage.
+template <int D, bool TAN>
+__device__ __forceinline__ void value_block(const uint4 *v_tile, const uint4 *dv_tile,
+                                            const bf16x8 *pb, const bf16x8 *pdsb, f32x16 *accO,
+                                            f32x16 *accT) {
+  constexpr int KCH = Geo<D>::KCH, DT = Geo<D>::DT;
+  const int lane = threadIdx.x & 63;
+  const int hh = lane >> 5;
   const int g = lane >> 4, jl = lane & 15;
   // (held across the key loop by every kernel: these are few)
   const int dcol = 16 * (g & 1) + 4 * (jl & 3);
@@ -374,11 +410,11 @@ __device__ __forceinline__ void softmax_value_block(const StageTile<D> *st, f32x
       for (int half = 0; half < 2; ++half) {
         const int key = 16 * s + 4 * half + krel;
         const int chunk = key * KCH + ((d >> 3) ^ v_swz<D>(key));
-        const char *vp = reinterpret_cast<const char *>(st->v + chunk) + (d & 7) * 2;
+        const char *vp = reinterpret_cast<const char *>(v_tile + chunk) + (d & 7) * 2;
         vh[half] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
             (__attribute__((address_space(3))) bf16x4 *)(vp));
         if (TAN) {
-          const char *dvp = reinterpret_cast<const char *>(st->dv + chunk) + (d & 7) * 2;
+          const char *dvp = reinterpret_cast<const char *>(dv_tile + chunk) + (d & 7) * 2;
           dvh[half] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
               (__attribute__((address_space(3))) bf16x4 *)(dvp));
         }
@@ -398,6 +434,19 @@ __device__ __forceinline__ void softmax_value_block(const StageTile<D> *st, f32x
   }
 }
 
+// Masking, online-softmax update and value step of one key block.
+template <int D, bool TAN>
+__device__ __forceinline__ void softmax_value_block(const StageTile<D, TAN> *st, f32x16 S, f32x16 dS,
+                                                    f32x16 *accO, f32x16 *accT, float &m_ref,
+                                                    float &l_run, float &mu_run, bool partial,
+                                                    int row_in_tile, float scale_log2,
+                                                    float scale) {
+  bf16x8 pb[2], pdsb[2];
+  softmax_block<D, TAN>(&st->bits[row_in_tile], S, dS, accO, accT, m_ref, l_run, mu_run, partial,
+                        scale_log2, scale, pb, pdsb);
+  value_block<D, TAN>(st->v, dv_tile(st), pb, pdsb, accO, accT);
+}
+
 // Waves per SIMD: two (one workgroup per CU), or four (two workgroups per
 // CU) for the head-dim-64 primal kernel, which fits in 128 VGPRs without a
 // spill (24 % faster; the kernels that would spill at 128 run 20-26 % slower).
@@ -409,7 +458,7 @@ __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<D, TAN>, kWavesPerSimd<D, TAN>)))
 void attn_jvp_bf16_wide_kernel(KernelParams p) {
   constexpr int KCH = Geo<D>::KCH, KSTEPS = Geo<D>::KSTEPS, DT = Geo<D>::DT;
-  using Stage = StageTile<D>;
+  using Stage = StageTile<D, TAN>;
   __shared__ Stage ring[kStages];
   __shared__ uint4 dq_lds[TAN ? BM * KCH : 1];
   __shared__ int2 ents[2][kEntChunk];
