@@ -20,7 +20,8 @@ __all__ = [
     "AttnJvpError", "Mask", "attn_jvp_mask_tf", "attn_jvp_mask_rects", "attn_jvp_mask_dense",
     "attn_jvp_mask_info", "attn_jvp_mask_export", "attn_jvp_mask_schedule", "attn_jvp_mask_free",
     "attn_jvp_mask_block_causal", "attn_jvp_mask_transpose", "attn_jvp_mask_split_schedule",
-    "attn_jvp_fwd", "attn_jvp_fwd_split_workspace", "attn_jvp_split_choose", "attn_jvp_bwd", "attn_jvp_tile_shape",
+    "attn_jvp_fwd", "attn_jvp_fwd_split_workspace", "attn_jvp_split_choose",
+    "attn_jvp_fwd_split_noalloc", "attn_jvp_bwd", "attn_jvp_tile_shape",
     "attn_jvp_status_str", "attn_jvp_version",
 ]
 
@@ -292,6 +293,42 @@ def attn_jvp_fwd(q, k, v, dq, dk, dv, mask, scale=None, o=None, d_o=None, lse=No
                                       ctypes.c_uint64(nbytes), ctypes.c_void_p(handle))
             _check(st, "attn_jvp_fwd_split")
     if want_dlse:
+        return o, (d_o if tangent else None), lse, d_lse
+    return o, (d_o if tangent else None), lse
+
+
+def attn_jvp_fwd_split_noalloc(q, k, v, dq, dk, dv, mask, o, lse, d_o=None, d_lse=None,
+                               max_splits=2, scale=None, stream=None):
+    """The split-key forward with the library's fixed scratch array in place
+    of a workspace (see attn_jvp.h): allocates nothing, so the outputs o, lse
+    (and d_o with any tangent, d_lse if wanted) must be given.  The mask's
+    schedule for this device and max_splits must be resident (one earlier
+    attn_jvp_fwd with the same max_splits makes it so).  Layout rules as for
+    attn_jvp_fwd.  Returns (o, d_o, lse), plus d_lse when given."""
+    import torch
+    tangent = dq is not None or dk is not None or dv is not None
+    if not q.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    for name, t in (("o", o), ("lse", lse)) + ((("d_o", d_o),) if tangent else ()):
+        if t is None:
+            raise ValueError(f"{name} must be given: this call allocates nothing")
+    B, n_q, H, D = q.shape
+    ptr = lambda t: t.data_ptr() if t is not None else None
+    a = _lib.AttnJvpArgs(
+        dtype=_dtype_code(q), B=B, H=H, n_q=n_q, n_k=k.shape[1], D=D,
+        q=ptr(q), k=ptr(k), v=ptr(v), dq=ptr(dq), dk=ptr(dk), dv=ptr(dv),
+        o=ptr(o), d_o=ptr(d_o) if tangent else None, lse=ptr(lse),
+        q_stride_b=q.stride(0), q_stride_n=q.stride(1), q_stride_h=q.stride(2),
+        k_stride_b=k.stride(0), k_stride_n=k.stride(1), k_stride_h=k.stride(2),
+        scale=float(scale) if scale is not None else 0.0, d_lse=ptr(d_lse))
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    with torch.cuda.device(q.device):
+        st = _lib.lib().attn_jvp_fwd_split_noalloc(ctypes.byref(a), mask.handle, int(max_splits),
+                                                   ctypes.c_void_p(handle))
+    _check(st, "attn_jvp_fwd_split_noalloc")
+    if d_lse is not None:
         return o, (d_o if tangent else None), lse, d_lse
     return o, (d_o if tangent else None), lse
 

@@ -18,6 +18,9 @@ ATTN_JVP_ERR_MASK = -5
 ATTN_JVP_ERR_UNSUPPORTED = -6
 ATTN_JVP_ERR_HIP = -7
 ATTN_JVP_ERR_OOM = -8
+ATTN_JVP_ERR_NOT_READY = -9
+ATTN_JVP_ERR_SCRATCH = -10
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 ATTN_JVP_BF16 = 0
 ATTN_JVP_F32 = 1
@@ -72,6 +75,7 @@ SIGNATURES = {
     "attn_jvp_fwd_split_workspace": (_i32, [ctypes.POINTER(AttnJvpArgs), _p, _i32,
                                             ctypes.POINTER(ctypes.c_uint64)]),
     "attn_jvp_fwd_split": (_i32, [ctypes.POINTER(AttnJvpArgs), _p, _i32, _p, ctypes.c_uint64, _p]),
+    "attn_jvp_fwd_split_noalloc": (_i32, [ctypes.POINTER(AttnJvpArgs), _p, _i32, _p]),
     "attn_jvp_split_choose": (_i32, [ctypes.POINTER(AttnJvpArgs), _p, _i32, _pi32]),
     "attn_jvp_bwd": (_i32, [ctypes.POINTER(AttnJvpBwdArgs), _p, _p]),
     "attn_jvp_tile_shape": (_i32, [_i32, _i32, _pi32, _pi32]),

@@ -84,13 +84,18 @@ bool reachable(const Term *t, int n, __int128 L, __int128 U, bool nonzero, int64
   return false;
 }
 
+// At most two extents of three strided dimensions meet in a search.
+constexpr int kMaxTerms = 6;
+
 // Normalises the terms (positive coefficients, fixed terms folded into the
 // target, terms of equal coefficient merged: x + y over two ranges takes
 // every value of the summed range) and runs the search.  Only for the
-// existence of a solution, so not with the nonzero condition.
-bool search(std::vector<Term> terms, __int128 L, __int128 U) {
-  std::vector<Term> live;
-  for (Term t : terms) {
+// existence of a solution, so not with the nonzero condition.  No heap use.
+bool search(const Term *terms, int n_terms, __int128 L, __int128 U) {
+  Term live[kMaxTerms];
+  int n = 0;
+  for (int i = 0; i < n_terms; ++i) {
+    Term t = terms[i];
     if (t.c < 0) t = {-t.c, -t.hi, -t.lo};
     if (t.c == 0 || t.hi == t.lo) {
       L -= t.c * t.lo;
@@ -98,49 +103,51 @@ bool search(std::vector<Term> terms, __int128 L, __int128 U) {
       continue;
     }
     bool merged = false;
-    for (Term &u : live)
-      if (u.c == t.c) {
-        u.lo += t.lo;
-        u.hi += t.hi;
+    for (int k = 0; k < n; ++k)
+      if (live[k].c == t.c) {
+        live[k].lo += t.lo;
+        live[k].hi += t.hi;
         merged = true;
       }
-    if (!merged) live.push_back(t);
+    if (!merged) live[n++] = t;
   }
-  std::sort(live.begin(), live.end(), [](const Term &a, const Term &b) { return a.c > b.c; });
+  std::sort(live, live + n, [](const Term &a, const Term &b) { return a.c > b.c; });
   int64_t budget = 1 << 20;
-  return reachable(live.data(), int(live.size()), L, U, false, &budget);
+  return reachable(live, n, L, U, false, &budget);
 }
 
 // Do two extents share a byte?  (Exact unless the search budget runs out,
 // which answers yes.)
 bool extents_overlap(const Extent &a, const Extent &b) {
   if (!a.base || !b.base || a.width <= 0 || b.width <= 0) return false;
-  std::vector<Term> t;
-  for (int k = 0; k < a.n; ++k) t.push_back({a.stride[k], 0, a.count[k] - 1});
-  for (int k = 0; k < b.n; ++k) t.push_back({-__int128(b.stride[k]), 0, b.count[k] - 1});
+  Term t[kMaxTerms];
+  int n = 0;
+  for (int k = 0; k < a.n; ++k) t[n++] = {a.stride[k], 0, a.count[k] - 1};
+  for (int k = 0; k < b.n; ++k) t[n++] = {-__int128(b.stride[k]), 0, b.count[k] - 1};
   const __int128 d = __int128(reinterpret_cast<uintptr_t>(b.base)) -
                      __int128(reinterpret_cast<uintptr_t>(a.base));
   // a + sa + e == b + sb + f  <=>  sa - sb == d + f - e, f - e in (-wa, wb)
-  return search(t, d - (a.width - 1), d + (b.width - 1));
+  return search(t, n, d - (a.width - 1), d + (b.width - 1));
 }
 
 // Do two different index tuples of one extent share a byte (a view that
 // writes some element twice)?
 bool extent_self_overlaps(const Extent &a) {
   if (!a.base || a.width <= 0) return false;
-  std::vector<Term> t;
+  Term t[kMaxTerms];
+  int n = 0;
   for (int k = 0; k < a.n; ++k) {
     if (a.count[k] < 2) continue;
     const int64_t c = a.stride[k] < 0 ? -a.stride[k] : a.stride[k];
     // a zero stride, or two strides of one size, give one address twice
     if (c == 0) return true;
-    for (const Term &u : t)
-      if (u.c == c) return true;
-    t.push_back({c, -(a.count[k] - 1), a.count[k] - 1});
+    for (int i = 0; i < n; ++i)
+      if (t[i].c == c) return true;
+    t[n++] = {c, -(a.count[k] - 1), a.count[k] - 1};
   }
-  std::sort(t.begin(), t.end(), [](const Term &x, const Term &y) { return x.c > y.c; });
+  std::sort(t, t + n, [](const Term &x, const Term &y) { return x.c > y.c; });
   int64_t budget = 1 << 20;
-  return reachable(t.data(), int(t.size()), -(a.width - 1), a.width - 1, true, &budget);
+  return reachable(t, n, -(a.width - 1), a.width - 1, true, &budget);
 }
 
 // Outputs must not share a byte with any input, with another output or with
@@ -529,9 +536,14 @@ extern "C" int attn_jvp_split_choose(const attn_jvp_args *a, const attn_jvp_mask
   return ATTN_JVP_OK;
 }
 
-extern "C" int attn_jvp_fwd_split(const attn_jvp_args *a, const attn_jvp_mask *m,
-                                  int32_t max_splits, void *workspace, uint64_t workspace_bytes,
-                                  void *stream) {
+// The split-key launch on a given workspace (see attn_jvp_fwd_split).  With
+// resident_only, nothing is built, uploaded or allocated: the mask's unit
+// list and its device copies for this device must already be cached
+// (ERR_NOT_READY otherwise), and a workspace smaller than the launch needs is
+// ERR_SCRATCH rather than ERR_SHAPE.
+int attnjvp::fwd_split(const attn_jvp_args *a, const attn_jvp_mask *m, int32_t max_splits,
+                       void *workspace, uint64_t workspace_bytes, void *stream,
+                       bool resident_only) {
   bool tangent = false;
   int st = validate_fwd(a, m, &tangent);
   if (st != ATTN_JVP_OK) return st;
@@ -542,14 +554,22 @@ extern "C" int attn_jvp_fwd_split(const attn_jvp_args *a, const attn_jvp_mask *m
   int64_t need = 0, n_units = 0, n_split = 0;
   {
     std::lock_guard<std::mutex> lock(m->mu);
-    const attnjvp::HostSplit *h = attnjvp::host_split_locked(m, BM, BN, max_splits, &st);
-    if (!h) return st;
+    const attnjvp::HostSplit *h = nullptr;
+    if (resident_only) {
+      auto it = m->host_split.find(std::make_tuple(BM, BN, int(max_splits)));
+      if (it == m->host_split.end()) return ATTN_JVP_ERR_NOT_READY;
+      h = &it->second;
+    } else {
+      h = attnjvp::host_split_locked(m, BM, BN, max_splits, &st);
+      if (!h) return st;
+    }
     need = split_workspace_bytes(a, BM, h->n_parts);
     n_units = h->n_units;
     n_split = int64_t(h->split_tiles.size() / 4);
   }
   if (need > 0 && !workspace) return ATTN_JVP_ERR_NULL;
-  if (uint64_t(need) > workspace_bytes) return ATTN_JVP_ERR_SHAPE;
+  if (uint64_t(need) > workspace_bytes)
+    return resident_only ? ATTN_JVP_ERR_SCRATCH : ATTN_JVP_ERR_SHAPE;
   const int64_t slices = int64_t(a->B) * a->H;
   if (n_units * slices > int64_t(0x7fffffff) || n_split * slices * BM > int64_t(0x7fffffff))
     return ATTN_JVP_ERR_SHAPE;
@@ -579,10 +599,18 @@ extern "C" int attn_jvp_fwd_split(const attn_jvp_args *a, const attn_jvp_mask *m
   const attnjvp::DeviceSplit *sp = nullptr;
   {
     std::lock_guard<std::mutex> lock(m->mu);
-    st = device_schedule_locked(m, device, BM, BN, &ds);
-    if (st != ATTN_JVP_OK) return st;
-    st = device_split_locked(m, device, BM, BN, max_splits, &sp);
-    if (st != ATTN_JVP_OK) return st;
+    if (resident_only) {
+      auto is = m->dev_sched.find(std::make_tuple(device, BM, BN));
+      auto ip = m->dev_split.find(std::make_tuple(device, BM, BN, int(max_splits)));
+      if (is == m->dev_sched.end() || ip == m->dev_split.end()) return ATTN_JVP_ERR_NOT_READY;
+      ds = &is->second;
+      sp = &ip->second;
+    } else {
+      st = device_schedule_locked(m, device, BM, BN, &ds);
+      if (st != ATTN_JVP_OK) return st;
+      st = device_split_locked(m, device, BM, BN, max_splits, &sp);
+      if (st != ATTN_JVP_OK) return st;
+    }
   }
 
   KernelParams p = fwd_params(a, tangent, ds);
@@ -612,6 +640,12 @@ extern "C" int attn_jvp_fwd_split(const attn_jvp_args *a, const attn_jvp_mask *m
   mp.n_parts = sp->n_parts;
   const int err = attnjvp::launch_merge(mp, a->D, a->dtype == ATTN_JVP_BF16, tangent, stream);
   return err == hipSuccess ? ATTN_JVP_OK : ATTN_JVP_ERR_HIP;
+}
+
+extern "C" int attn_jvp_fwd_split(const attn_jvp_args *a, const attn_jvp_mask *m,
+                                  int32_t max_splits, void *workspace, uint64_t workspace_bytes,
+                                  void *stream) {
+  return attnjvp::fwd_split(a, m, max_splits, workspace, workspace_bytes, stream, false);
 }
 
 extern "C" int attn_jvp_bwd(const attn_jvp_bwd_args *a, const attn_jvp_mask *m, void *stream) {
@@ -721,6 +755,11 @@ extern "C" const char *attn_jvp_status_str(int status) {
     case ATTN_JVP_ERR_UNSUPPORTED: return "unsupported configuration";
     case ATTN_JVP_ERR_HIP: return "HIP device unavailable or HIP call failed";
     case ATTN_JVP_ERR_OOM: return "out of memory";
+    case ATTN_JVP_ERR_NOT_READY:
+      return "mask schedule not resident on this device for this split count (run "
+             "attn_jvp_fwd_split once first)";
+    case ATTN_JVP_ERR_SCRATCH:
+      return "launch needs more workspace than the fixed scratch buffer holds";
     default: return "unknown status";
   }
 }

@@ -20,7 +20,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 
 SOURCES = ["attn_jvp_mask.cpp", "attn_jvp_api.cpp", "attn_jvp_bf16_wide.hip",
            "attn_jvp_f32.hip", "attn_jvp_merge.hip", "attn_jvp_bwd_wide.hip",
-           "attn_jvp_bwd_f32.hip"]
+           "attn_jvp_bwd_f32.hip", "attn_jvp_noalloc.hip"]
 ARCH = "gfx950"
 
 COMMON = [

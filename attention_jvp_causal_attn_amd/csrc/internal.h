@@ -217,6 +217,13 @@ int split_schedule(const HostSchedule &s, int max_splits, HostSplit *out);
 const HostSplit *host_split_locked(const attn_jvp_mask *m, int block_m, int block_n,
                                    int max_splits, int *status);
 
+// The split-key launch of attn_jvp_fwd_split on a given workspace; with
+// resident_only it builds, uploads and allocates nothing (ERR_NOT_READY when
+// the mask's split schedule is not cached for this device, ERR_SCRATCH when
+// the workspace is too small).
+int fwd_split(const attn_jvp_args *a, const attn_jvp_mask *m, int32_t max_splits,
+              void *workspace, uint64_t workspace_bytes, void *stream, bool resident_only);
+
 // Kernel launchers (defined in the .hip files).  Return a hipError_t value.
 int launch_bf16(const KernelParams &p, int D, bool tangent, void *stream);
 int launch_bwd_bf16_wide(const BwdParams &p, int D, void *stream);

@@ -57,7 +57,12 @@ enum attn_jvp_status {
                                     aliasing outputs, the LSE tangent
                                     without any input tangent) */
   ATTN_JVP_ERR_HIP = -7,         /* no usable HIP device, or a HIP call failed */
-  ATTN_JVP_ERR_OOM = -8          /* host or device allocation failed */
+  ATTN_JVP_ERR_OOM = -8,         /* host or device allocation failed */
+  ATTN_JVP_ERR_NOT_READY = -9,   /* allocation-free call: the mask's schedule
+                                    for this device and split count is not
+                                    resident yet */
+  ATTN_JVP_ERR_SCRATCH = -10     /* allocation-free call: the launch needs more
+                                    than the fixed scratch buffer */
 };
 
 enum attn_jvp_dtype {
@@ -242,6 +247,28 @@ int attn_jvp_fwd_split_workspace(const attn_jvp_args *a, const attn_jvp_mask *m,
 int attn_jvp_fwd_split(const attn_jvp_args *a, const attn_jvp_mask *m,
                        int32_t max_splits, void *workspace,
                        uint64_t workspace_bytes, void *hip_stream);
+
+/* attn_jvp_fwd_split without any allocation, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  Same arguments (less the workspace) and
+ * results, bit for bit, as attn_jvp_fwd_split with the same max_splits: the
+ * partial sums of cut tiles go to a fixed scratch array of
+ * ATTN_JVP_NOALLOC_SCRATCH_BYTES bytes that the library holds on every device
+ * it runs on until the process ends.  The call allocates nothing, host or
+ * device, and builds and uploads nothing: the mask's schedule and unit list
+ * for this device, tile shape and max_splits must already be resident, which
+ * one earlier attn_jvp_fwd_split call with the same max_splits on this device
+ * (any arguments with the same dtype and D) makes them.  Nothing in the
+ * scratch needs clearing.  All calls on one device share its scratch array:
+ * calls that may overlap in time (on different streams, or from several
+ * threads without ordering) race and give wrong results; order them on one
+ * stream.  Errors: those of attn_jvp_fwd_split, ERR_NOT_READY (schedule not
+ * resident), ERR_SCRATCH (the workspace attn_jvp_fwd_split_workspace reports
+ * for these arguments exceeds ATTN_JVP_NOALLOC_SCRATCH_BYTES), ERR_HIP (the
+ * scratch array's address could not be obtained). */
+#define ATTN_JVP_NOALLOC_SCRATCH_BYTES (64ull << 20)
+int attn_jvp_fwd_split_noalloc(const attn_jvp_args *a, const attn_jvp_mask *m,
+                               int32_t max_splits, void *hip_stream);
 
 /* A max_splits for attn_jvp_fwd_split on a device with n_cu compute units
  * (host-only: nothing is launched).  Returns 1 when the unsplit grid has at

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     assert aj.attn_jvp_version() == 1
-    for st in range(-8, 1):
+    for st in range(-10, 1):
         assert aj.attn_jvp_status_str(st) not in ("", "unknown status")
     assert aj.attn_jvp_status_str(-99) == "unknown status"
     assert aj.attn_jvp_tile_shape(aj.ATTN_JVP_BF16, 128) == (256, 32)
@@ -167,6 +167,18 @@ def test_split_without_device_reports_hip_error():
     a = _args(mask)
     assert _split(a, mask, 1) == _lib.ATTN_JVP_ERR_HIP
     assert _split(a, mask, 2, 1 << 40, 1 << 30) == _lib.ATTN_JVP_ERR_HIP
+
+
+def test_noalloc_argument_checks():
+    mask = aj.attn_jvp_mask_tf(4, 16, 1)
+    L = _lib.lib()
+    assert L.attn_jvp_fwd_split_noalloc(None, mask.handle, 2, None) == _lib.ATTN_JVP_ERR_NULL
+    a = _args(mask)
+    assert L.attn_jvp_fwd_split_noalloc(ctypes.byref(a), None, 2, None) == _lib.ATTN_JVP_ERR_NULL
+    if not _gpu_present():
+        # no device: the scratch array has no address to fetch
+        assert L.attn_jvp_fwd_split_noalloc(ctypes.byref(a), mask.handle, 2, None) == \
+            _lib.ATTN_JVP_ERR_HIP
 
 
 def test_fwd_null_args_and_mask():
