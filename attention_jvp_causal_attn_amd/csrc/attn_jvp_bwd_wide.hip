@@ -295,6 +295,15 @@ void bwd_dq_wide_kernel(BwdParams p) {
 #pragma unroll
   for (int nt = 0; nt < DT; ++nt) acc[nt] = f32x16{};
   const float sl2 = p.scale_log2;
+  // dP^T - D accumulates from -D: the MFMA chain starts from these registers
+  // (kept for the tile), so the subtraction costs no instruction per block
+  // (head dim 128 only: the head-dim-64 pass must fit 128 registers)
+  constexpr bool kInitD = D == 128;
+  f32x16 g_init = {};
+  if constexpr (kInitD) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) g_init[r] = -dsum;
+  }
 
   // Per-lane LDS read offsets, held across the key loop (registers allow it
   // in this pass); the loop below is unrolled by two so that the ring stage
@@ -312,7 +321,7 @@ void bwd_dq_wide_kernel(BwdParams p) {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     const int2 ent = entry(j);
-    f32x16 S = {}, G = {};
+    f32x16 S = {}, G = g_init;
 #pragma unroll
     for (int t = 0; t < KSTEPS; ++t) {
       S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(st->k, krow, t, hh), qf[t], S, 0, 0, 0);
@@ -332,7 +341,8 @@ void bwd_dq_wide_kernel(BwdParams p) {
       for (int r = 0; r < 16; ++r) x[r] = (bits >> reg_pos(r)) & 1u ? x[r] : -__builtin_inff();
     }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) gs[r] = __builtin_amdgcn_exp2f(x[r]) * (G[r] - dsum);
+    for (int r = 0; r < 16; ++r)
+      gs[r] = __builtin_amdgcn_exp2f(x[r]) * (kInitD ? G[r] : G[r] - dsum);
     bf16x8 gsb[2];
     gsb[0] = to_bf16x8(gs);
     gsb[1] = to_bf16x8(gs + 8);
@@ -458,6 +468,19 @@ void bwd_dkv_wide_kernel(BwdParams p) {
 #pragma unroll
     for (int t = 0; t < KSTEPS; ++t) kf[t] = as_bf16x8(*reinterpret_cast<const uint4 *>(kp + 16 * t));
   }
+  // The staged V rows are negated in place (each lane flips the sign bits of
+  // the chunks its own copies wrote, once they have landed), so that the
+  // per-block MFMA chain H = D + g (-V)^T, started from the queries' D,
+  // gives D - dP without a subtraction per element.
+  wait_vmcnt<0>();
+#pragma unroll
+  for (int i = 0; i < BM * KCH / kThreads; ++i) {
+    uint4 *c = v_lds + i * kThreads + threadIdx.x;
+    uint4 x = *c;
+    x.x ^= 0x80008000u; x.y ^= 0x80008000u; x.z ^= 0x80008000u; x.w ^= 0x80008000u;
+    *c = x;
+  }
+  wait_lgkmcnt0();  // published by the first block's barrier
 
   f32x16 accK[DT], accV[DT];
 #pragma unroll
@@ -491,7 +514,25 @@ void bwd_dkv_wide_kernel(BwdParams p) {
       asm volatile("" : "+v"(qperm));
     }
     const uint4 *vrow = v_lds + key_in_tile * KCH;
-    f32x16 S = {}, G = {};
+    // LSE and D of this lane's 16 queries 8hh + {0..7} and 16 + 8hh + {0..7}
+    // (query q sits in region q / 4 at slot q % 4 (LSE) and 4 + q % 4 (D));
+    // element r of the score tile holds query r of that list, so D goes
+    // straight into the accumulator that H = D - dP starts from
+    float lq[16];
+    f32x16 G;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+      for (int rg = 0; rg < 2; ++rg) {
+        const float4 *reg = reinterpret_cast<const float4 *>(st->ld + 8 * (4 * half + 2 * hh + rg));
+        const float4 a = reg[0], b = reg[1];
+        lq[8 * half + 4 * rg + 0] = a.x; lq[8 * half + 4 * rg + 1] = a.y;
+        lq[8 * half + 4 * rg + 2] = a.z; lq[8 * half + 4 * rg + 3] = a.w;
+        G[8 * half + 4 * rg + 0] = b.x; G[8 * half + 4 * rg + 1] = b.y;
+        G[8 * half + 4 * rg + 2] = b.z; G[8 * half + 4 * rg + 3] = b.w;
+      }
+    }
+    f32x16 S = {};
     if constexpr (kHoist) {
 #pragma unroll
       for (int t = 0; t < KSTEPS; ++t) {
@@ -515,21 +556,6 @@ void bwd_dkv_wide_kernel(BwdParams p) {
       }
     }
     if (j + 1 < n) issue(next_stage, entry(j + 1));  // its stage was released by the barrier
-    // LSE and D of this lane's 16 queries 8hh + {0..7} and 16 + 8hh + {0..7}:
-    // query q sits in region q / 4 at slot q % 4 (LSE) and 4 + q % 4 (D)
-    float lq[16], dq[16];
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-#pragma unroll
-      for (int rg = 0; rg < 2; ++rg) {
-        const float4 *reg = reinterpret_cast<const float4 *>(st->ld + 8 * (4 * half + 2 * hh + rg));
-        const float4 a = reg[0], b = reg[1];
-        lq[8 * half + 4 * rg + 0] = a.x; lq[8 * half + 4 * rg + 1] = a.y;
-        lq[8 * half + 4 * rg + 2] = a.z; lq[8 * half + 4 * rg + 3] = a.w;
-        dq[8 * half + 4 * rg + 0] = b.x; dq[8 * half + 4 * rg + 1] = b.y;
-        dq[8 * half + 4 * rg + 2] = b.z; dq[8 * half + 4 * rg + 3] = b.w;
-      }
-    }
     // partial block: scores of inadmissible pairs to -inf (scale > 0), whose
     // probability exp2 then makes exactly 0, and the LSE of a query without
     // keys (-inf) to 0 so that its pairs, all inadmissible, stay at exp2(-inf);
@@ -541,13 +567,13 @@ void bwd_dkv_wide_kernel(BwdParams p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) lq[e] = lq[e] == -__builtin_inff() ? 0.f : lq[e];
     }
+    // element r holds query r of the lane's list (8 (pos / 16) + pos % 8 = r
+    // for pos = reg_pos(r)); gs = P (D - dP) = -dS, so dK is negated at the end
     float pr[16], gs[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int pos = reg_pos(r);
-      const int e = 8 * (pos >> 4) + (pos & 7);
-      pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], sl2, -lq[e] * kLog2e));
-      gs[r] = pr[r] * (G[r] - dq[e]);
+      pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], sl2, -lq[r] * kLog2e));
+      gs[r] = pr[r] * G[r];
     }
     bf16x8 pb[2], gsb[2];
     pb[0] = to_bf16x8(pr);
@@ -585,7 +611,7 @@ void bwd_dkv_wide_kernel(BwdParams p) {
       float xk[4], xv[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        xk[i] = accK[nt][4 * jj + i] * p.scale;
+        xk[i] = accK[nt][4 * jj + i] * -p.scale;  // the accumulated -dS
         xv[i] = accV[nt][4 * jj + i];
       }
       *reinterpret_cast<uint2 *>(gk + d0) = make_uint2(pack_bf16(xk[0], xk[1]), pack_bf16(xk[2], xk[3]));
