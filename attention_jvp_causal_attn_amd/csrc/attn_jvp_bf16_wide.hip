@@ -266,14 +266,10 @@ __device__ __forceinline__ bf16x8 row_read(const uint4 *row, int t, int hh, int 
     return as_bf16x8(row[(2 * t + hh) ^ x]);
 }
 
-// The tangent tiles of a stage (JVP kernels only).
+// The dK tile of a stage (JVP kernels only).
 template <int D, bool TAN>
 __device__ __forceinline__ const uint4 *dk_tile(const StageTile<D, TAN> *st) {
   if constexpr (TAN) return st->dk; else return nullptr;
-}
-template <int D, bool TAN>
-__device__ __forceinline__ const uint4 *dv_tile(const StageTile<D, TAN> *st) {
-  if constexpr (TAN) return st->dv; else return nullptr;
 }
 
 // S^T = K Q^T and dS^T = K dQ^T + dK Q^T; Q from registers, dQ from LDS.
@@ -293,6 +289,17 @@ __device__ __forceinline__ void score_block(const StageTile<D, TAN> *st, const u
   const uint32_t ky = 16u * uint32_t(hh ^ kx), qy = 16u * uint32_t(hh ^ qx);
   S = f32x16{};
   dS = f32x16{};
+  if constexpr (!TAN) {
+    // primal: every K operand of the block read up front (registers allow)
+    bf16x8 kfs[KSTEPS];
+#pragma unroll
+    for (int t = 0; t < KSTEPS; ++t) kfs[t] = row_read<kXad>(Ks, t, hh, kx, ky);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < KSTEPS; ++t)
+      S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfs[t], qf[t], S, 0, 0, 0);
+    return;
+  }
 #pragma unroll
   for (int t = 0; t < KSTEPS; ++t) {
     const bf16x8 kf = row_read<kXad>(Ks, t, hh, kx, ky);
@@ -310,18 +317,17 @@ __device__ __forceinline__ void score_block(const StageTile<D, TAN> *st, const u
   }
 }
 
-// Masking and online-softmax update of one key block: the block's weights P
-// (and P * dS) rounded to bf16 for the value MFMAs, l and mu updated, the
-// accumulators rescaled when the reference max moves.
+// Masking of a partial block (inadmissible scores to -inf and, with a
+// tangent, their score tangents to 0), the block's row max, and the shared
+// rescale of the running sums and accumulators when the reference max moves
+// by more than the slack.  Returns the reference max the weights use.
 template <int D, bool TAN>
-__device__ __forceinline__ void softmax_block(const uint32_t *bits_row, f32x16 S, f32x16 dS,
-                                              f32x16 *accO, f32x16 *accT, float &m_ref,
-                                              float &l_run, float &mu_run, bool partial,
-                                              float scale_log2, float scale, bf16x8 *pb,
-                                              bf16x8 *pdsb) {
+__device__ __forceinline__ float mask_and_rescale(const uint32_t *bits_row, f32x16 &S, f32x16 &dS,
+                                                  f32x16 *accO, f32x16 *accT, float &m_ref,
+                                                  float &l_run, float &mu_run, bool partial,
+                                                  float scale_log2) {
   constexpr int DT = Geo<D>::DT;
-  const int lane = threadIdx.x & 63;
-  const int hh = lane >> 5;
+  const int hh = (threadIdx.x & 63) >> 5;
   if (partial) {
     // this lane-half's keys 8hh + {0..7, 16..23}, so the bit positions below
     // are constants
@@ -353,85 +359,148 @@ __device__ __forceinline__ void softmax_block(const uint32_t *bits_row, f32x16 S
     }
     m_ref = m_new;
   }
-  const float m_use = m_ref == kNegInf ? 0.f : m_ref;
-  float pr[16], pds[16];
-  // l and mu are summed from the bf16 weights the value MFMAs consume, two
-  // per v_dot2 (half the vector instructions of fp32 sums, and O, dO are then
-  // normalised by exactly the weights they were accumulated with)
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], scale_log2, -m_use));
-    if (TAN) pds[r] = pr[r] * (dS[r] * scale);
-  }
-  pb[0] = to_bf16x8(pr);
-  pb[1] = to_bf16x8(pr + 8);
-  if (TAN) {
-    pdsb[0] = to_bf16x8(pds);
-    pdsb[1] = to_bf16x8(pds + 8);
-  }
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-  float lsum = 0.f, musum = 0.f;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bf16x2 pp = {pb[h][2 * i], pb[h][2 * i + 1]};
-      lsum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lsum, false);
-      if (TAN) {
-        const bf16x2 qq = {pdsb[h][2 * i], pdsb[h][2 * i + 1]};
-        musum = __builtin_amdgcn_fdot2_f32_bf16(qq, ones, musum, false);
-      }
-    }
-  }
-  l_run += lsum;
-  if (TAN) mu_run += musum;
+  return m_ref == kNegInf ? 0.f : m_ref;
 }
 
-// Value step of one key block: A^T += V^T P^T, and with tangents
-// T^T += V^T (P*dS)^T + dV^T P^T, V and dV read transposed from the stage.
-template <int D, bool TAN>
-__device__ __forceinline__ void value_block(const uint4 *v_tile, const uint4 *dv_tile,
-                                            const bf16x8 *pb, const bf16x8 *pdsb, f32x16 *accO,
-                                            f32x16 *accT) {
-  constexpr int KCH = Geo<D>::KCH, DT = Geo<D>::DT;
+// The V^T operands of a block's value step: within each group of 16 lanes,
+// lane jl reads keys 16s + 4half + krel at dims d0 + 4(jl % 4) .. +3,
+// transposed by ds_read_b64_tr_b16.
+template <int D>
+__device__ __forceinline__ bf16x8 v_operand(const uint4 *v_tile, int s, int nt) {
+  constexpr int KCH = Geo<D>::KCH;
   const int lane = threadIdx.x & 63;
-  const int hh = lane >> 5;
   const int g = lane >> 4, jl = lane & 15;
-  // (held across the key loop by every kernel: these are few)
   const int dcol = 16 * (g & 1) + 4 * (jl & 3);
-  const int krel = 8 * hh + (jl >> 2);
+  const int krel = 8 * (lane >> 5) + (jl >> 2);
+  const int d = 32 * nt + dcol;
+  bf16x4 vh[2];
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
+  for (int half = 0; half < 2; ++half) {
+    const int key = 16 * s + 4 * half + krel;
+    const int chunk = key * KCH + ((d >> 3) ^ v_swz<D>(key));
+    const char *vp = reinterpret_cast<const char *>(v_tile + chunk) + (d & 7) * 2;
+    vh[half] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (__attribute__((address_space(3))) bf16x4 *)(vp));
+  }
+  return __builtin_shufflevector(vh[0], vh[1], 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// l (and mu) summed from the bf16 weights the value MFMAs consume, two per
+// v_dot2 (half the vector instructions of fp32 sums, and O, dO are then
+// normalised by exactly the weights they were accumulated with).
+__device__ __forceinline__ float sum_bf16x8(const bf16x8 &w, float acc) {
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bf16x2 pp = {w[2 * i], w[2 * i + 1]};
+    acc = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, acc, false);
+  }
+  return acc;
+}
+
+// Primal: every V operand of the block is read before the softmax (its LDS
+// latency hides behind it; the registers allow it), then the weights, then
+// A^T += V^T P^T.
+template <int D>
+__device__ __forceinline__ void softmax_value_primal(const StageTile<D, false> *st, f32x16 S,
+                                                     f32x16 *accO, float &m_ref, float &l_run,
+                                                     bool partial, int row_in_tile,
+                                                     float scale_log2) {
+  constexpr int DT = Geo<D>::DT;
+  bf16x8 vf[2][DT];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int nt = 0; nt < DT; ++nt) vf[s][nt] = v_operand<D>(st->v, s, nt);
+  __builtin_amdgcn_sched_barrier(0);
+  f32x16 no_dS;
+  float no_mu = 0.f;
+  const float m_use = mask_and_rescale<D, false>(&st->bits[row_in_tile], S, no_dS, accO, nullptr,
+                                                 m_ref, l_run, no_mu, partial, scale_log2);
+  float pr[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], scale_log2, -m_use));
+  bf16x8 pb[2];
+  pb[0] = to_bf16x8(pr);
+  pb[1] = to_bf16x8(pr + 8);
+  l_run += sum_bf16x8(pb[1], sum_bf16x8(pb[0], 0.f));
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int nt = 0; nt < DT; ++nt)
+      accO[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[s][nt], pb[s], accO[nt], 0, 0, 0);
+}
+
+// JVP (head dim 128): mask and rescale over the block, the weights P and
+// P*dS of keys 0-15, then their value MFMAs (A^T += V^T P^T, T^T += V^T (P*dS)^T + dV^T P^T)
+// interleaved two vector instructions per MFMA with the weights of keys
+// 16-31, then those of keys 16-31 with the l and mu sums: the matrix core
+// works while the second half of the softmax runs.  The sums see the same
+// operations in the same order as a plain softmax-then-MFMA block.
+template <int D>
+__device__ __forceinline__ void softmax_value_jvp(const StageTile<D, true> *st, f32x16 S,
+                                                  f32x16 dS, f32x16 *accO, f32x16 *accT,
+                                                  float &m_ref, float &l_run, float &mu_run,
+                                                  bool partial, int row_in_tile, float scale_log2,
+                                                  float scale) {
+  constexpr int DT = Geo<D>::DT;
+  const float m_use = mask_and_rescale<D, true>(&st->bits[row_in_tile], S, dS, accO, accT, m_ref,
+                                                l_run, mu_run, partial, scale_log2);
+  auto weights = [&](int h, bf16x8 &pb, bf16x8 &pdsb) __attribute__((always_inline)) {
+    float pr[8], pds[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[8 * h + r], scale_log2, -m_use));
+      pds[r] = pr[r] * (dS[8 * h + r] * scale);
+    }
+    pb = to_bf16x8(pr);
+    pdsb = to_bf16x8(pds);
+  };
+  auto value_step = [&](int s, const bf16x8 &pb, const bf16x8 &pdsb) __attribute__((always_inline)) {
 #pragma unroll
     for (int nt = 0; nt < DT; ++nt) {
-      const int d = 32 * nt + dcol;
-      bf16x4 vh[2], dvh[2];
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int key = 16 * s + 4 * half + krel;
-        const int chunk = key * KCH + ((d >> 3) ^ v_swz<D>(key));
-        const char *vp = reinterpret_cast<const char *>(v_tile + chunk) + (d & 7) * 2;
-        vh[half] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (__attribute__((address_space(3))) bf16x4 *)(vp));
-        if (TAN) {
-          const char *dvp = reinterpret_cast<const char *>(dv_tile + chunk) + (d & 7) * 2;
-          dvh[half] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-              (__attribute__((address_space(3))) bf16x4 *)(dvp));
-        }
-      }
-      const bf16x8 vf = __builtin_shufflevector(vh[0], vh[1], 0, 1, 2, 3, 4, 5, 6, 7);
-      accO[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[s], accO[nt], 0, 0, 0);
-      if (TAN) {
-        const bf16x8 dvf = __builtin_shufflevector(dvh[0], dvh[1], 0, 1, 2, 3, 4, 5, 6, 7);
-        accT[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pdsb[s], accT[nt], 0, 0, 0);
-        accT[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dvf, pb[s], accT[nt], 0, 0, 0);
-      }
-      // bound the operand prefetch: every two dim tiles, or at head dim 128
-      // with tangents every four (0.4 % faster there)
-      constexpr int kFence = (D == 128 && TAN) ? 4 : 2;
-      if (nt % kFence == kFence - 1) __builtin_amdgcn_sched_barrier(0);
+      const bf16x8 vf = v_operand<D>(st->v, s, nt);
+      const bf16x8 dvf = v_operand<D>(st->dv, s, nt);
+      accO[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb, accO[nt], 0, 0, 0);
+      accT[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pdsb, accT[nt], 0, 0, 0);
+      accT[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dvf, pb, accT[nt], 0, 0, 0);
     }
+  };
+  bf16x8 pb0, pdsb0, pb1, pdsb1;
+  if constexpr (D == 64) {
+    // head dim 64 (half the MFMAs per block): the plain order is faster
+    // (the interleaved one measured 1 % slower)
+    weights(0, pb0, pdsb0);
+    weights(1, pb1, pdsb1);
+    l_run += sum_bf16x8(pb1, sum_bf16x8(pb0, 0.f));
+    mu_run += sum_bf16x8(pdsb1, sum_bf16x8(pdsb0, 0.f));
+    value_step(0, pb0, pdsb0);
+    __builtin_amdgcn_sched_barrier(0);
+    value_step(1, pb1, pdsb1);
+    __builtin_amdgcn_sched_barrier(0);
+    return;
   }
+  weights(0, pb0, pdsb0);
+  __builtin_amdgcn_sched_barrier(0);
+  value_step(0, pb0, pdsb0);
+  weights(1, pb1, pdsb1);
+#pragma unroll
+  for (int i = 0; i < 3 * DT; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // two vector instructions
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  value_step(1, pb1, pdsb1);
+  const float lsum = sum_bf16x8(pb1, sum_bf16x8(pb0, 0.f));
+  const float musum = sum_bf16x8(pdsb1, sum_bf16x8(pdsb0, 0.f));
+#pragma unroll
+  for (int i = 0; i < 3 * DT; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  l_run += lsum;
+  mu_run += musum;
 }
 
 // Masking, online-softmax update and value step of one key block.
@@ -441,10 +510,11 @@ __device__ __forceinline__ void softmax_value_block(const StageTile<D, TAN> *st,
                                                     float &l_run, float &mu_run, bool partial,
                                                     int row_in_tile, float scale_log2,
                                                     float scale) {
-  bf16x8 pb[2], pdsb[2];
-  softmax_block<D, TAN>(&st->bits[row_in_tile], S, dS, accO, accT, m_ref, l_run, mu_run, partial,
-                        scale_log2, scale, pb, pdsb);
-  value_block<D, TAN>(st->v, dv_tile(st), pb, pdsb, accO, accT);
+  if constexpr (TAN)
+    softmax_value_jvp<D>(st, S, dS, accO, accT, m_ref, l_run, mu_run, partial, row_in_tile,
+                         scale_log2, scale);
+  else
+    softmax_value_primal<D>(st, S, accO, m_ref, l_run, partial, row_in_tile, scale_log2);
 }
 
 // Waves per SIMD: two (one workgroup per CU), or four (two workgroups per
