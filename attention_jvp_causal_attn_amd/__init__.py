@@ -179,9 +179,12 @@ def attn_jvp_mask_free(mask):
     mask.free()
 
 
-def attn_jvp_tile_shape(dtype, D):
+def attn_jvp_tile_shape(dtype, D, tangent=True):
+    """(block_m, block_n) of the forward kernel for (dtype, D), with or
+    without input tangents (see attn_jvp.h)."""
     bm, bn = ctypes.c_int32(), ctypes.c_int32()
-    _check(_lib.lib().attn_jvp_tile_shape(int(dtype), int(D), ctypes.byref(bm), ctypes.byref(bn)),
+    _check(_lib.lib().attn_jvp_tile_shape(int(dtype), int(D), int(bool(tangent)),
+                                          ctypes.byref(bm), ctypes.byref(bn)),
            "attn_jvp_tile_shape")
     return bm.value, bn.value
 

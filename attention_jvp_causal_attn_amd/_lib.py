@@ -78,7 +78,7 @@ SIGNATURES = {
     "attn_jvp_fwd_split_noalloc": (_i32, [ctypes.POINTER(AttnJvpArgs), _p, _i32, _p]),
     "attn_jvp_split_choose": (_i32, [ctypes.POINTER(AttnJvpArgs), _p, _i32, _pi32]),
     "attn_jvp_bwd": (_i32, [ctypes.POINTER(AttnJvpBwdArgs), _p, _p]),
-    "attn_jvp_tile_shape": (_i32, [_i32, _i32, _pi32, _pi32]),
+    "attn_jvp_tile_shape": (_i32, [_i32, _i32, _i32, _pi32, _pi32]),
     "attn_jvp_status_str": (ctypes.c_char_p, [_i32]),
     "attn_jvp_version": (_i32, []),
 }

@@ -308,13 +308,15 @@ extern "C" void attn_jvp_mask_free(attn_jvp_mask *m) {
   delete m;
 }
 
-extern "C" int attn_jvp_tile_shape(int32_t dtype, int32_t D, int32_t *block_m, int32_t *block_n) {
+extern "C" int attn_jvp_tile_shape(int32_t dtype, int32_t D, int32_t tangent, int32_t *block_m,
+                                   int32_t *block_n) {
   if (!block_m || !block_n) return ATTN_JVP_ERR_NULL;
   if (dtype != ATTN_JVP_BF16 && dtype != ATTN_JVP_F32) return ATTN_JVP_ERR_DTYPE;
   if (D != 64 && D != 128) return ATTN_JVP_ERR_UNSUPPORTED;
   if (dtype == ATTN_JVP_BF16) {
     *block_m = attnjvp::kBf16BlockMWide;
-    *block_n = attnjvp::kBf16BlockN;
+    // the head-dim-128 primal-only kernel works through 64-key blocks
+    *block_n = (!tangent && D == 128) ? attnjvp::kBf16BlockNPrimal128 : attnjvp::kBf16BlockN;
   } else {
     *block_m = attnjvp::kF32BlockM;
     *block_n = attnjvp::kF32BlockN;
@@ -435,7 +437,7 @@ extern "C" int attn_jvp_fwd(const attn_jvp_args *a, const attn_jvp_mask *m, void
   int device = -1;
   if (hipGetDevice(&device) != hipSuccess) return ATTN_JVP_ERR_HIP;
   int BM = 0, BN = 0;
-  attn_jvp_tile_shape(a->dtype, a->D, &BM, &BN);
+  attn_jvp_tile_shape(a->dtype, a->D, tangent, &BM, &BN);
   const DeviceSchedule *ds = nullptr;
   {
     std::lock_guard<std::mutex> lock(m->mu);
@@ -461,7 +463,7 @@ extern "C" int attn_jvp_fwd_split_workspace(const attn_jvp_args *a, const attn_j
   if (st != ATTN_JVP_OK) return st;
   if (max_splits < 1) return ATTN_JVP_ERR_SHAPE;
   int BM = 0, BN = 0;
-  attn_jvp_tile_shape(a->dtype, a->D, &BM, &BN);
+  attn_jvp_tile_shape(a->dtype, a->D, tangent, &BM, &BN);
   std::lock_guard<std::mutex> lock(m->mu);
   const attnjvp::HostSplit *h = attnjvp::host_split_locked(m, BM, BN, max_splits, &st);
   if (!h) return st;
@@ -503,7 +505,7 @@ extern "C" int attn_jvp_split_choose(const attn_jvp_args *a, const attn_jvp_mask
   if (st != ATTN_JVP_OK) return st;
   if (n_cu < 1) return ATTN_JVP_ERR_SHAPE;
   int BM = 0, BN = 0;
-  attn_jvp_tile_shape(a->dtype, a->D, &BM, &BN);
+  attn_jvp_tile_shape(a->dtype, a->D, tangent, &BM, &BN);
   // workgroups resident per compute unit: one for the bf16 kernels (their
   // registers fill the SIMDs) but the head-dim-64 primal one (four waves per
   // SIMD: two), two for the fp32 kernel
@@ -550,7 +552,7 @@ int attnjvp::fwd_split(const attn_jvp_args *a, const attn_jvp_mask *m, int32_t m
   if (max_splits < 1) return ATTN_JVP_ERR_SHAPE;
   if (workspace && !aligned16(workspace)) return ATTN_JVP_ERR_ALIGN;
   int BM = 0, BN = 0;
-  attn_jvp_tile_shape(a->dtype, a->D, &BM, &BN);
+  attn_jvp_tile_shape(a->dtype, a->D, tangent, &BM, &BN);
   int64_t need = 0, n_units = 0, n_split = 0;
   {
     std::lock_guard<std::mutex> lock(m->mu);

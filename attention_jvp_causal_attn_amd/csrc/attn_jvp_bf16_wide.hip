@@ -84,6 +84,14 @@ struct Geo {
   static constexpr int TILE = BN * KCH;  // chunks of one 32-row tile
 };
 
+// Keys per block: 32, or 64 for the head-dim-128 primal kernel (two score
+// tiles per block: half the barriers and per-block scalar work per key, and
+// two independent score chains).  The host builds the schedule for the same
+// width (attn_jvp_tile_shape).
+template <int D, bool TAN>
+constexpr int kBlockN = (!TAN && D == 128) ? 64 : 32;
+static_assert(kBlockN<128, false> == kBf16BlockNPrimal128, "host and kernel block widths");
+
 template <int D, bool TAN>
 struct alignas(16) StageTile {
   uint4 k[Geo<D>::TILE];
@@ -94,9 +102,10 @@ struct alignas(16) StageTile {
 };
 template <int D>
 struct alignas(16) StageTile<D, false> {  // primal: no tangent tiles
-  uint4 k[Geo<D>::TILE];
-  uint4 v[Geo<D>::TILE];
-  uint32_t bits[BM];
+  static constexpr int W = kBlockN<D, false> / 32;  // mask words per row
+  uint4 k[W * Geo<D>::TILE];
+  uint4 v[W * Geo<D>::TILE];
+  uint32_t bits[BM * W];
 };
 // LDS byte offset of tensor t (0 K, 1 V, 2 dK, 3 dV) inside a stage.
 template <int D, bool TAN>
@@ -203,8 +212,22 @@ __device__ __forceinline__ void issue_block(uint32_t st, int wave, const KernelP
   const int64_t boff = int64_t(key0) * p.k_sn;
   // rebuilt per block (cheaper than holding them in registers); rows past n_k
   // re-read the last key, masked out by the schedule
-  const int rows_valid = min(BN, p.n_k - key0);
-  if constexpr (D == 128) {
+  const int rows_valid = min(kBlockN<D, TAN>, p.n_k - key0);
+  if constexpr (kBlockN<D, TAN> == 64) {
+    // 64 rows of K and V: two copies per tensor per wave; mask bits: BM x 2
+    // words = 128 chunks, wave w copies chunks 16w .. 16w+15 (lanes 0..15)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const DmaOffsets o = dma_offsets<D>(i * kThreads + int(threadIdx.x), p.k_sn, rows_valid);
+      const uint32_t chunk = uint32_t(i * kThreads + wave * 64) * 16u;
+      dma16(kb_ + boff, o.k, st + uint32_t(offsetof(ST, k)) + chunk);
+      dma16(vb_ + boff, o.v, st + uint32_t(offsetof(ST, v)) + chunk);
+    }
+    if (lane < 16)
+      dma16(bits_src, uint32_t(wave * 16 + lane) * 16u,
+            st + uint32_t(offsetof(ST, bits)) + uint32_t(wave) * 256u);
+    return;
+  } else if constexpr (D == 128) {
     // one copy per tensor per wave, all at this lane's chunk: one offset pair
     // serves the four tensors (the general loop below compiles slower here)
     const DmaOffsets o = dma_offsets<D>(int(threadIdx.x), p.k_sn, rows_valid);
@@ -503,6 +526,98 @@ __device__ __forceinline__ void softmax_value_jvp(const StageTile<D, true> *st, 
   mu_run += musum;
 }
 
+// Primal kernel with 64-key blocks: S0^T = K[0:32] Q^T and S1^T = K[32:64] Q^T
+// as two interleaved MFMA chains (every K operand read first), then the mask,
+// max and rescale over both tiles, the weights, and A^T += V^T P^T over four
+// 16-key steps (the V operands of the first two read before the softmax).
+template <int D>
+__device__ __forceinline__ void score_primal64(const StageTile<D, false> *st, const bf16x8 *qf,
+                                               f32x16 &S0, f32x16 &S1) {
+  constexpr int KCH = Geo<D>::KCH, KSTEPS = Geo<D>::KSTEPS;
+  const int lane = threadIdx.x & 63;
+  const int col = lane & 31, hh = lane >> 5;
+  const int krow = swap_bits23(col);
+  const int kx = k_swz<D>(krow);
+  const uint4 *K0 = st->k + krow * KCH, *K1 = st->k + (32 + krow) * KCH;
+  bf16x8 k0[KSTEPS], k1[KSTEPS];
+#pragma unroll
+  for (int t = 0; t < KSTEPS; ++t) {
+    k0[t] = as_bf16x8(K0[(2 * t + hh) ^ kx]);
+    k1[t] = as_bf16x8(K1[(2 * t + hh) ^ kx]);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  S0 = f32x16{};
+  S1 = f32x16{};
+#pragma unroll
+  for (int t = 0; t < KSTEPS; ++t) {
+    S0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0[t], qf[t], S0, 0, 0, 0);
+    S1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1[t], qf[t], S1, 0, 0, 0);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void softmax_value_primal64(const StageTile<D, false> *st, f32x16 S0,
+                                                       f32x16 S1, f32x16 *accO, float &m_ref,
+                                                       float &l_run, bool partial,
+                                                       int row_in_tile, float scale_log2) {
+  constexpr int DT = Geo<D>::DT;
+  const int hh = (threadIdx.x & 63) >> 5;
+  bf16x8 vf[2][DT];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int nt = 0; nt < DT; ++nt) vf[s][nt] = v_operand<D>(st->v, s, nt);
+  __builtin_amdgcn_sched_barrier(0);
+  if (partial) {
+    // this lane-half's keys 8hh + {0..7, 16..23} of each 32-key tile
+    const uint32_t b0 = st->bits[2 * row_in_tile] >> (8 * hh);
+    const uint32_t b1 = st->bits[2 * row_in_tile + 1] >> (8 * hh);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int j = r >> 2, i = r & 3;
+      const int key = 16 * (j >> 1) + 4 * (j & 1) + i;
+      S0[r] = (b0 >> key) & 1u ? S0[r] : kNegInf;
+      S1[r] = (b1 >> key) & 1u ? S1[r] : kNegInf;
+    }
+  }
+  float mh = fmaxf(S0[0], S1[0]);
+#pragma unroll
+  for (int r = 1; r < 16; ++r) mh = fmaxf(mh, fmaxf(S0[r], S1[r]));
+  mh *= scale_log2;
+  if (__builtin_amdgcn_ballot_w64(mh > m_ref + kRescaleSlack) != 0) {
+    const float mx = fmaxf(mh, xor32(mh));
+    const bool grow = mx > m_ref + kRescaleSlack;
+    const float m_new = grow ? mx : m_ref;
+    const float alpha = grow ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.f;
+    l_run *= alpha;
+#pragma unroll
+    for (int nt = 0; nt < DT; ++nt) accO[nt] *= alpha;
+    m_ref = m_new;
+  }
+  const float m_use = m_ref == kNegInf ? 0.f : m_ref;
+  float pr[32];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S0[r], scale_log2, -m_use));
+    pr[16 + r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S1[r], scale_log2, -m_use));
+  }
+  bf16x8 pb[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) pb[s] = to_bf16x8(pr + 8 * s);
+  l_run += sum_bf16x8(pb[3], sum_bf16x8(pb[2], sum_bf16x8(pb[1], sum_bf16x8(pb[0], 0.f))));
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int nt = 0; nt < DT; ++nt)
+      accO[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[s][nt], pb[s], accO[nt], 0, 0, 0);
+#pragma unroll
+  for (int s = 2; s < 4; ++s)
+#pragma unroll
+    for (int nt = 0; nt < DT; ++nt)
+      accO[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_operand<D>(st->v, s, nt), pb[s],
+                                                         accO[nt], 0, 0, 0);
+}
+
 // Masking, online-softmax update and value step of one key block.
 template <int D, bool TAN>
 __device__ __forceinline__ void softmax_value_block(const StageTile<D, TAN> *st, f32x16 S, f32x16 dS,
@@ -570,8 +685,9 @@ void attn_jvp_bf16_wide_kernel(KernelParams p) {
     const int2 e = ents[(j / kEntChunk) & 1][j % kEntChunk];
     return make_int2(__builtin_amdgcn_readfirstlane(e.x), __builtin_amdgcn_readfirstlane(e.y));
   };
+  constexpr int BNK = kBlockN<D, TAN>;  // keys per block
   auto bits_of = [&](int2 ent) {
-    return p.partial_bits + int64_t(ent.y >= 0 ? ent.y : p.n_partial) * BM;
+    return p.partial_bits + int64_t(ent.y >= 0 ? ent.y : p.n_partial) * (BM * BNK / 32);
   };
 
   load_entries(0);
@@ -580,7 +696,7 @@ void attn_jvp_bf16_wide_kernel(KernelParams p) {
   int2 ent_c = n > 0 ? entry(0) : no_ent;
   int2 ent_1 = n > 1 ? entry(1) : no_ent;
   if (n > 0)
-    issue_block<D, TAN>(stage_lds(0), wave, p, kb_, dkb_, vb_, dvb_, ent_c.x * BN, bits_of(ent_c));
+    issue_block<D, TAN>(stage_lds(0), wave, p, kb_, dkb_, vb_, dvb_, ent_c.x * BNK, bits_of(ent_c));
 
   // dQ tile -> LDS (rows past n_q re-read the last row), Q -> registers.
   if (TAN) {
@@ -633,13 +749,20 @@ void attn_jvp_bf16_wide_kernel(KernelParams p) {
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
       f32x16 S, dS;
-      score_block<D, TAN>(st, dq_lds, qf, row_in_tile, S, dS);
+      if constexpr (BNK == 64)
+        score_primal64<D>(st, qf, S, dS);  // (the two score tiles)
+      else
+        score_block<D, TAN>(st, dq_lds, qf, row_in_tile, S, dS);
       // block j + 1 into the other stage (released by the barrier)
       if (j + 1 < n)
-        issue_block<D, TAN>(stage_lds(next_stage), wave, p, kb_, dkb_, vb_, dvb_, ent_1.x * BN,
+        issue_block<D, TAN>(stage_lds(next_stage), wave, p, kb_, dkb_, vb_, dvb_, ent_1.x * BNK,
                          bits_of(ent_1));
-      softmax_value_block<D, TAN>(st, S, dS, accO, accT, m_ref, l_run, mu_run, ent_c.y >= 0,
-                               row_in_tile, p.scale_log2, p.scale);
+      if constexpr (BNK == 64)
+        softmax_value_primal64<D>(st, S, dS, accO, m_ref, l_run, ent_c.y >= 0, row_in_tile,
+                                  p.scale_log2);
+      else
+        softmax_value_block<D, TAN>(st, S, dS, accO, accT, m_ref, l_run, mu_run, ent_c.y >= 0,
+                                    row_in_tile, p.scale_log2, p.scale);
       ent_c = ent_1;
       ent_1 = j + 2 < n ? entry(j + 2) : no_ent;
     };

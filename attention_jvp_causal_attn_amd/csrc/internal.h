@@ -234,6 +234,7 @@ int launch_merge(const MergeParams &p, int D, bool bf16, bool tangent, void *str
 // Tile shapes of the kernels.
 constexpr int kBf16BlockMWide = 256;  // 8 waves x 32 rows (head dims 64 and 128)
 constexpr int kBf16BlockN = 32;
+constexpr int kBf16BlockNPrimal128 = 64;  // head-dim-128 primal-only kernel
 constexpr int kBwdBlockMWide = 256;   // backward: 8 waves x 32 rows (or keys)
 constexpr int kBwdBlockN = 32;        // backward: blocks of 32 keys (or queries)
 constexpr int kF32BlockM = 64;

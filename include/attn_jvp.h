@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define ATTN_JVP_API_VERSION 1
+#define ATTN_JVP_API_VERSION 2
 
 enum attn_jvp_status {
   ATTN_JVP_OK = 0,
@@ -316,10 +316,12 @@ typedef struct attn_jvp_bwd_args {
 int attn_jvp_bwd(const attn_jvp_bwd_args *a, const attn_jvp_mask *m,
                  void *hip_stream);
 
-/* Tile shape (query rows, keys) the kernel for (dtype, D) uses; these are the
- * block_m / block_n of its schedule.  Errors: ERR_NULL, ERR_DTYPE,
- * ERR_UNSUPPORTED (D not 64 or 128). */
-int attn_jvp_tile_shape(int32_t dtype, int32_t D, int32_t *block_m,
+/* Tile shape (query rows, keys per block) of the forward kernel for (dtype,
+ * D) with (tangent != 0) or without (tangent == 0) input tangents; these are
+ * the block_m / block_n of the schedule that kernel walks (the bf16 primal-only
+ * kernel at D = 128 takes 64-key blocks, every other bf16 kernel 32).
+ * Errors: ERR_NULL, ERR_DTYPE, ERR_UNSUPPORTED (D not 64 or 128). */
+int attn_jvp_tile_shape(int32_t dtype, int32_t D, int32_t tangent, int32_t *block_m,
                         int32_t *block_n);
 
 /* Static English text for a status code (never NULL). */

@@ -101,7 +101,8 @@ int main(void) {
   int32_t chosen = 0;
   CHECK(attn_jvp_split_choose(&args, m, 256, &chosen) == ATTN_JVP_OK && chosen >= 1);
   int32_t bm = 0, bn = 0;
-  CHECK(attn_jvp_tile_shape(ATTN_JVP_BF16, 128, &bm, &bn) == ATTN_JVP_OK && bm == 256 && bn == 32);
+  CHECK(attn_jvp_tile_shape(ATTN_JVP_BF16, 128, 1, &bm, &bn) == ATTN_JVP_OK && bm == 256 && bn == 32);
+  CHECK(attn_jvp_tile_shape(ATTN_JVP_BF16, 128, 0, &bm, &bn) == ATTN_JVP_OK && bm == 256 && bn == 64);
 
   attn_jvp_bwd_args bargs;
   memset(&bargs, 0, sizeof(bargs));

@@ -31,13 +31,16 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert aj.attn_jvp_version() == 1
+    assert aj.attn_jvp_version() == 2
     for st in range(-10, 1):
         assert aj.attn_jvp_status_str(st) not in ("", "unknown status")
     assert aj.attn_jvp_status_str(-99) == "unknown status"
     assert aj.attn_jvp_tile_shape(aj.ATTN_JVP_BF16, 128) == (256, 32)
+    assert aj.attn_jvp_tile_shape(aj.ATTN_JVP_BF16, 128, tangent=False) == (256, 64)
     assert aj.attn_jvp_tile_shape(aj.ATTN_JVP_BF16, 64) == (256, 32)
+    assert aj.attn_jvp_tile_shape(aj.ATTN_JVP_BF16, 64, tangent=False) == (256, 32)
     assert aj.attn_jvp_tile_shape(aj.ATTN_JVP_F32, 64) == (64, 32)
+    assert aj.attn_jvp_tile_shape(aj.ATTN_JVP_F32, 128, tangent=False) == (64, 32)
     with pytest.raises(aj.AttnJvpError):
         aj.attn_jvp_tile_shape(aj.ATTN_JVP_BF16, 96)
     with pytest.raises(aj.AttnJvpError):

@@ -170,8 +170,9 @@ def test_full_size_schedule_covers_visible_pairs(nf, tpf, fpc):
     # Every admissible pair is covered exactly once by the scheduled blocks.
     m = aj.attn_jvp_mask_tf(nf, tpf, fpc)
     info = m.info()
-    for dtype in (aj.ATTN_JVP_BF16, aj.ATTN_JVP_F32):
-        BM, BN = aj.attn_jvp_tile_shape(dtype, 128)
+    for dtype, tangent in ((aj.ATTN_JVP_BF16, True), (aj.ATTN_JVP_BF16, False),
+                           (aj.ATTN_JVP_F32, True)):
+        BM, BN = aj.attn_jvp_tile_shape(dtype, 128, tangent)
         s = aj.attn_jvp_mask_schedule(m, BM, BN)
         n_q, n_k = info["n_q"], info["n_k"]
         total = 0
