@@ -22,12 +22,14 @@
 //    and dK^T += Q^T dS.
 // Eight waves per workgroup, two per SIMD, 32 rows (or keys) each: one
 // wave's softmax-side vector work runs while the other keeps the matrix core
-// busy.  Every value lives in the 256 VGPRs a wave has at two waves per
+// busy; at head dim 128 the two waves of a SIMD are held half a block apart
+// (one forms a block's scores while the other finishes the previous block's
+// gradient update), over a 3-stage ring.  Every value lives in the 256 VGPRs a wave has at two waves per
 // SIMD; the dK/dV pass therefore stages its V rows in LDS (read as the MFMA
 // B operand) while K stays in registers.  Both passes use one lane per row
 // in each half-wave, the row permutation that puts a lane's 8 weights of a
-// 16-wide step in register order, direct-to-LDS copies into a 2-stage ring
-// (block j + 1 is copied while block j is computed), and tiles swizzled so
+// 16-wide step in register order, direct-to-LDS copies into a ring (block
+// j + 1 is copied while block j is computed), and tiles swizzled so
 // that both row reads (ds_read_b128) and transposed reads
 // (ds_read_b64_tr_b16) hit distinct banks.
 #include <hip/hip_runtime.h>
@@ -205,6 +207,13 @@ __device__ __forceinline__ TrLane tr_lane() {
   return {16 * (g & 1) + 4 * (jl & 3), 8 * (lane >> 5) + (jl >> 2)};
 }
 
+// Head dim 128 (both passes): the two waves of a SIMD run half a block apart
+// over a 3-stage ring.  Head dim 64 keeps one phase and 2 stages (its dQ pass
+// runs four waves per SIMD within 128 registers, which the carried scores
+// would exceed).
+template <int D>
+constexpr bool kPingPong = D == 128;
+
 // ---------------------------------------------------------------- dQ pass
 
 template <int D>
@@ -225,7 +234,7 @@ __attribute__((amdgpu_waves_per_eu(kDqWavesPerSimd<D>, kDqWavesPerSimd<D>)))
 void bwd_dq_wide_kernel(BwdParams p) {
   constexpr int KSTEPS = Geo<D>::KSTEPS, DT = Geo<D>::DT;
   using KVTile = attnjvp::KVTile<D>;
-  __shared__ KVTile ring[2];
+  __shared__ KVTile ring[kPingPong<D> ? 3 : 2];
   __shared__ int2 ents[2][kEntChunk];
   const int L = work_item(int(blockIdx.x), p.r_map);
   const int slot = L % p.r_map.n_tiles;
@@ -310,25 +319,19 @@ void bwd_dq_wide_kernel(BwdParams p) {
   // of every read is an immediate offset.
   const int krow = swap_bits23(col);
   const TrLane tl = tr_lane();
-  // One block: S^T, dP^T, dS^T and the dQ update.
-  auto step = [&](int j, const KVTile *st, int next_stage) __attribute__((always_inline)) {
-    if ((j + 1) % kEntChunk == 0 && j + 1 < n) {
-      // the next chunk of entries, read after this barrier (entry(j + 1))
-      load_entries((j + 1) / kEntChunk);
-      wait_lgkmcnt0();
-    }
-    wait_vmcnt<0>();  // block j (and, first time, Q, g, O) has landed
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    const int2 ent = entry(j);
-    f32x16 S = {}, G = g_init;
+  // A block in two halves.  h1: S^T and dP^T - D (MFMAs from the block's K, V
+  // rows).  h2: exponents, mask, dS^T and the dQ update (K^T read transposed).
+  auto h1 = [&](const KVTile *st, f32x16 &S, f32x16 &G) __attribute__((always_inline)) {
+    S = f32x16{};
+    G = g_init;
 #pragma unroll
     for (int t = 0; t < KSTEPS; ++t) {
       S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(st->k, krow, t, hh), qf[t], S, 0, 0, 0);
       G = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(st->v, krow, t, hh), gf[t], G, 0, 0, 0);
       if (t % 4 == 3) __builtin_amdgcn_sched_barrier(0);  // bound the operand prefetch
     }
-    if (j + 1 < n) issue(next_stage, entry(j + 1));  // its stage was released by the barrier
+  };
+  auto h2 = [&](int2 ent, const KVTile *st, const f32x16 &S, const f32x16 &G) __attribute__((always_inline)) {
     // exponents; in a partial block those of inadmissible pairs become -inf
     // (exp2 then gives exactly 0, also for a row without keys, whose LSE is
     // -inf); full blocks skip the mask
@@ -356,9 +359,65 @@ void bwd_dq_wide_kernel(BwdParams p) {
       }
     }
   };
-  for (int j = 0; j < n; j += 2) {
-    step(j, &ring[0], 1);
-    if (j + 1 < n) step(j + 1, &ring[1], 0);
+  auto sync = [&](int j) __attribute__((always_inline)) {
+    if ((j + 1) % kEntChunk == 0 && j + 1 < n) {
+      // the next chunk of entries, read after this barrier (entry(j + 1))
+      load_entries((j + 1) / kEntChunk);
+      wait_lgkmcnt0();
+    }
+    wait_vmcnt<0>();  // block j (and, first time, Q, g, O) has landed
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  if constexpr (!kPingPong<D>) {
+    auto step = [&](int j, const KVTile *st, int next_stage) __attribute__((always_inline)) {
+      sync(j);
+      const int2 ent = entry(j);
+      f32x16 S, G;
+      h1(st, S, G);
+      if (j + 1 < n) issue(next_stage, entry(j + 1));  // its stage was released by the barrier
+      h2(ent, st, S, G);
+    };
+    for (int j = 0; j < n; j += 2) {
+      step(j, &ring[0], 1);
+      if (j + 1 < n) step(j + 1, &ring[1], 0);
+    }
+  } else if (wave < 4) {
+    // The two waves that share a SIMD (w and w + 4) run half a block apart:
+    // between two barriers, waves 0-3 do h1 and h2 of block j while waves 4-7
+    // do h2 of block j - 1 and h1 of block j, so one wave's vector work runs
+    // under the other's MFMAs.  Block j is read from its stage between
+    // barriers j and j + 2, hence a 3-stage ring; the copy for block j + 1,
+    // issued after barrier j, goes to the stage of block j - 2.
+    auto step = [&](int j, const KVTile *st, int next_stage) __attribute__((always_inline)) {
+      sync(j);
+      const int2 ent = entry(j);
+      f32x16 S, G;
+      h1(st, S, G);
+      if (j + 1 < n) issue(next_stage, entry(j + 1));  // its stage was released by the barrier
+      h2(ent, st, S, G);
+    };
+    for (int j = 0; j < n; j += 3) {
+      step(j, &ring[0], 1);
+      if (j + 1 < n) step(j + 1, &ring[1], 2);
+      if (j + 2 < n) step(j + 2, &ring[2], 0);
+    }
+  } else {
+    f32x16 S = {}, G = {};
+    int2 ent = make_int2(0, -1);
+    auto step = [&](int j, const KVTile *st, const KVTile *prev, int next_stage) __attribute__((always_inline)) {
+      sync(j);
+      if (j + 1 < n) issue(next_stage, entry(j + 1));
+      if (j > 0) h2(ent, prev, S, G);
+      ent = entry(j);
+      h1(st, S, G);
+    };
+    for (int j = 0; j < n; j += 3) {
+      step(j, &ring[0], &ring[2], 1);
+      if (j + 1 < n) step(j + 1, &ring[1], &ring[0], 2);
+      if (j + 2 < n) step(j + 2, &ring[2], &ring[1], 0);
+    }
+    if (n > 0) h2(ent, &ring[(n - 1) % 3], S, G);
   }
   wait_vmcnt<0>();
 
@@ -392,7 +451,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 void bwd_dkv_wide_kernel(BwdParams p) {
   constexpr int KCH = Geo<D>::KCH, KSTEPS = Geo<D>::KSTEPS, DT = Geo<D>::DT;
   using QGTile = attnjvp::QGTile<D>;
-  __shared__ QGTile ring[2];
+  __shared__ QGTile ring[kPingPong<D> ? 3 : 2];
   __shared__ uint4 v_lds[BM * KCH];  // this tile's V rows (B operands), 64 KB at D = 128
   __shared__ int2 ents[2][kEntChunk];
   const int L = work_item(int(blockIdx.x), p.c_map);
@@ -497,42 +556,30 @@ void bwd_dkv_wide_kernel(BwdParams p) {
   constexpr bool kHoist = D == 64;
   const int qperm_h = swap_bits23(col);
   const TrLane tl_h = tr_lane();
-  // One block of 32 queries: S, dP, dS and the dK, dV updates.
-  auto step = [&](int j, const QGTile *st, int next_stage) __attribute__((always_inline)) {
-    if ((j + 1) % kEntChunk == 0 && j + 1 < n) {
-      // the next chunk of entries, read after this barrier (entry(j + 1))
-      load_entries((j + 1) / kEntChunk);
-      wait_lgkmcnt0();
-    }
-    wait_vmcnt<0>();  // block j (and, first time, V and K) has landed
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    const int2 ent = entry(j);
+  // A block of 32 queries in two halves.  h1: S = Q K^T and H = D - dP
+  // (MFMAs from the block's Q, g rows).  h2: mask, P and -dS, then the dV, dK
+  // updates (transposed Q, g reads).
+  auto h1 = [&](const QGTile *st, f32x16 &S, f32x16 &G) __attribute__((always_inline)) {
     int qperm = qperm_h;
     if (!kHoist) {
       qperm = swap_bits23(col);
       asm volatile("" : "+v"(qperm));
     }
     const uint4 *vrow = v_lds + key_in_tile * KCH;
-    // LSE and D of this lane's 16 queries 8hh + {0..7} and 16 + 8hh + {0..7}
-    // (query q sits in region q / 4 at slot q % 4 (LSE) and 4 + q % 4 (D));
-    // element r of the score tile holds query r of that list, so D goes
-    // straight into the accumulator that H = D - dP starts from
-    float lq[16];
-    f32x16 G;
+    // D of this lane's 16 queries 8hh + {0..7} and 16 + 8hh + {0..7} (query q
+    // sits in region q / 4 at slot 4 + q % 4); element r of the score tile
+    // holds query r of that list, so D goes straight into the accumulator
+    // that H = D - dP starts from
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
 #pragma unroll
       for (int rg = 0; rg < 2; ++rg) {
-        const float4 *reg = reinterpret_cast<const float4 *>(st->ld + 8 * (4 * half + 2 * hh + rg));
-        const float4 a = reg[0], b = reg[1];
-        lq[8 * half + 4 * rg + 0] = a.x; lq[8 * half + 4 * rg + 1] = a.y;
-        lq[8 * half + 4 * rg + 2] = a.z; lq[8 * half + 4 * rg + 3] = a.w;
+        const float4 b = reinterpret_cast<const float4 *>(st->ld + 8 * (4 * half + 2 * hh + rg))[1];
         G[8 * half + 4 * rg + 0] = b.x; G[8 * half + 4 * rg + 1] = b.y;
         G[8 * half + 4 * rg + 2] = b.z; G[8 * half + 4 * rg + 3] = b.w;
       }
     }
-    f32x16 S = {};
+    S = f32x16{};
     if constexpr (kHoist) {
 #pragma unroll
       for (int t = 0; t < KSTEPS; ++t) {
@@ -555,7 +602,19 @@ void bwd_dkv_wide_kernel(BwdParams p) {
         if (t % 4 == 3) __builtin_amdgcn_sched_barrier(0);  // bound the operand prefetch
       }
     }
-    if (j + 1 < n) issue(next_stage, entry(j + 1));  // its stage was released by the barrier
+  };
+  auto h2 = [&](int2 ent, const QGTile *st, f32x16 S, const f32x16 &G) __attribute__((always_inline)) {
+    // LSE of the same 16 queries (slot q % 4 of region q / 4)
+    float lq[16];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+      for (int rg = 0; rg < 2; ++rg) {
+        const float4 a = reinterpret_cast<const float4 *>(st->ld + 8 * (4 * half + 2 * hh + rg))[0];
+        lq[8 * half + 4 * rg + 0] = a.x; lq[8 * half + 4 * rg + 1] = a.y;
+        lq[8 * half + 4 * rg + 2] = a.z; lq[8 * half + 4 * rg + 3] = a.w;
+      }
+    }
     // partial block: scores of inadmissible pairs to -inf (scale > 0), whose
     // probability exp2 then makes exactly 0, and the LSE of a query without
     // keys (-inf) to 0 so that its pairs, all inadmissible, stay at exp2(-inf);
@@ -593,9 +652,61 @@ void bwd_dkv_wide_kernel(BwdParams p) {
       }
     }
   };
-  for (int j = 0; j < n; j += 2) {
-    step(j, &ring[0], 1);
-    if (j + 1 < n) step(j + 1, &ring[1], 0);
+  auto sync = [&](int j) __attribute__((always_inline)) {
+    if ((j + 1) % kEntChunk == 0 && j + 1 < n) {
+      // the next chunk of entries, read after this barrier (entry(j + 1))
+      load_entries((j + 1) / kEntChunk);
+      wait_lgkmcnt0();
+    }
+    wait_vmcnt<0>();  // block j (and, first time, V and K) has landed
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  // Head dim 128 runs the two waves of a SIMD half a block apart, as the dQ
+  // pass does.
+  if constexpr (!kPingPong<D>) {
+    auto step = [&](int j, const QGTile *st, int next_stage) __attribute__((always_inline)) {
+      sync(j);
+      const int2 ent = entry(j);
+      f32x16 S, G;
+      h1(st, S, G);
+      if (j + 1 < n) issue(next_stage, entry(j + 1));  // its stage was released by the barrier
+      h2(ent, st, S, G);
+    };
+    for (int j = 0; j < n; j += 2) {
+      step(j, &ring[0], 1);
+      if (j + 1 < n) step(j + 1, &ring[1], 0);
+    }
+  } else if (wave < 4) {
+    auto step = [&](int j, const QGTile *st, int next_stage) __attribute__((always_inline)) {
+      sync(j);
+      const int2 ent = entry(j);
+      f32x16 S, G;
+      h1(st, S, G);
+      if (j + 1 < n) issue(next_stage, entry(j + 1));  // its stage was released by the barrier
+      h2(ent, st, S, G);
+    };
+    for (int j = 0; j < n; j += 3) {
+      step(j, &ring[0], 1);
+      if (j + 1 < n) step(j + 1, &ring[1], 2);
+      if (j + 2 < n) step(j + 2, &ring[2], 0);
+    }
+  } else {
+    f32x16 S = {}, G = {};
+    int2 ent = make_int2(0, -1);
+    auto step = [&](int j, const QGTile *st, const QGTile *prev, int next_stage) __attribute__((always_inline)) {
+      sync(j);
+      if (j + 1 < n) issue(next_stage, entry(j + 1));
+      if (j > 0) h2(ent, prev, S, G);
+      ent = entry(j);
+      h1(st, S, G);
+    };
+    for (int j = 0; j < n; j += 3) {
+      step(j, &ring[0], &ring[2], 1);
+      if (j + 1 < n) step(j + 1, &ring[1], &ring[0], 2);
+      if (j + 2 < n) step(j + 2, &ring[2], &ring[1], 0);
+    }
+    if (n > 0) h2(ent, &ring[(n - 1) % 3], S, G);
   }
   wait_vmcnt<0>();
 
