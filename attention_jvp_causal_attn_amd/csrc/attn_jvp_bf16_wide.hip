@@ -748,6 +748,11 @@ void attn_jvp_bf16_wide_kernel(KernelParams p) {
       wait_vmcnt<0>();  // block j (and, first time, dQ and Q) has landed
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
+      // the entry of block j + 2, read now (ahead of the operand reads) and
+      // made uniform at the end of the block, so that its LDS latency is not
+      // waited for just before the next barrier
+      // (past the last block it reads a placeholder or a stale slot, never used)
+      const int2 raw2 = ents[((j + 2) / kEntChunk) & 1][(j + 2) % kEntChunk];
       f32x16 S, dS;
       if constexpr (BNK == 64)
         score_primal64<D>(st, qf, S, dS);  // (the two score tiles)
@@ -764,7 +769,7 @@ void attn_jvp_bf16_wide_kernel(KernelParams p) {
         softmax_value_block<D, TAN>(st, S, dS, accO, accT, m_ref, l_run, mu_run, ent_c.y >= 0,
                                     row_in_tile, p.scale_log2, p.scale);
       ent_c = ent_1;
-      ent_1 = j + 2 < n ? entry(j + 2) : no_ent;
+      ent_1 = make_int2(__builtin_amdgcn_readfirstlane(raw2.x), __builtin_amdgcn_readfirstlane(raw2.y));
     };
     for (int j = 0; j < n; j += 2) {
       step(j, &ring[0], 1);
