@@ -340,6 +340,27 @@ __device__ __forceinline__ void score_block(const StageTile<D, TAN> *st, const u
   }
 }
 
+// max(a, b, c) as one v_max3_f32.  Through fmaxf the compiler first
+// quiets each MFMA result (one v_max_f32 x, x per score: it cannot know they
+// are not signalling NaNs) and then forms the tree from two-input maxima; the
+// scores here are finite or -inf, for which v_max3_f32 is the exact maximum.
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+// Maximum of n scores (n even) as a v_max3_f32 tree (used by the 64-key
+// primal kernel: 3.8 % faster there; the 32-key kernels, whose compiled max
+// has few such quieting moves, gain nothing).
+template <int n>
+__device__ __forceinline__ float max_of(const float *x) {
+  float m = max3(x[0], x[1], x[2]);
+#pragma unroll
+  for (int i = 3; i + 1 < n; i += 2) m = max3(m, x[i], x[i + 1]);
+  if constexpr (n % 2 == 0) m = max3(m, x[n - 1], x[n - 1]);
+  return m;
+}
+
 // Masking of a partial block (inadmissible scores to -inf and, with a
 // tangent, their score tangents to 0), the block's row max, and the shared
 // rescale of the running sums and accumulators when the reference max moves
@@ -580,10 +601,13 @@ __device__ __forceinline__ void softmax_value_primal64(const StageTile<D, false>
       S1[r] = (b1 >> key) & 1u ? S1[r] : kNegInf;
     }
   }
-  float mh = fmaxf(S0[0], S1[0]);
+  float sv[32];
 #pragma unroll
-  for (int r = 1; r < 16; ++r) mh = fmaxf(mh, fmaxf(S0[r], S1[r]));
-  mh *= scale_log2;
+  for (int r = 0; r < 16; ++r) {
+    sv[r] = S0[r];
+    sv[16 + r] = S1[r];
+  }
+  float mh = max_of<32>(sv) * scale_log2;
   if (__builtin_amdgcn_ballot_w64(mh > m_ref + kRescaleSlack) != 0) {
     const float mx = fmaxf(mh, xor32(mh));
     const bool grow = mx > m_ref + kRescaleSlack;
