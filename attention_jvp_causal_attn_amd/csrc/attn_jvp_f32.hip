@@ -7,11 +7,14 @@
 // precision products anywhere).  This path serves small fp32 problems; it is
 // not the throughput path.
 //
-// Layout: a workgroup of 256 threads owns 64 query rows of one (batch, head);
-// 4 consecutive lanes share a row, each holding D/4 of its dimensions of q,
-// dq and the two accumulators.  Key blocks of 32 rows of K, dK, V, dV are
-// staged in LDS; per key the 4 lanes reduce their partial dot products with
-// two xor-shuffles (every lane ends with the same bits).
+// Layout: a workgroup of 512 threads owns 64 query rows of one (batch, head);
+// 8 aligned lanes share a row, each holding D/8 of its dimensions of q, dq
+// and the two accumulators.  Key blocks of 32 rows of K, dK, V, dV are staged
+// in LDS and taken 16 keys at a time by the online softmax; per key the 8
+// lanes reduce their partial dot products in three DPP steps (every lane
+// ends with the same bits).  On small problems this path is bound by each
+// wave's chain of dependent vector instructions, which more lanes per row
+// (fewer dimensions each) shorten.
 #include <hip/hip_runtime.h>
 
 #include "internal.h"
@@ -19,12 +22,29 @@
 namespace attnjvp {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 constexpr int BM = kF32BlockM;  // 64 rows
-constexpr int BN = kF32BlockN;  // 32 keys
-constexpr int TPR = 4;          // lanes per row
-static_assert(BM * TPR == kThreads, "one row per 4 lanes");
+constexpr int BN = kF32BlockN;  // 32 keys per staged block
+constexpr int HB = 16;          // keys per online-softmax step
+constexpr int TPR = 8;          // lanes per row
+static_assert(BM * TPR == kThreads, "one row per 8 lanes");
 constexpr float kNegInf = -__builtin_inff();
+
+// DPP move within rows of 16 lanes (bound_ctrl off, all rows and banks).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+// Sum over the 8 aligned lanes of a row: add the value of lane l ^ 1 and
+// l ^ 2 (quad permutations), then of the lane mirrored within 8.  Each step
+// adds two sums of the same shape and a + b == b + a, so every lane ends
+// with the same bits.
+__device__ __forceinline__ float sum8(float x) {
+  x += dpp_mov<0xb1>(x);   // quad_perm [1, 0, 3, 2]
+  x += dpp_mov<0x4e>(x);   // quad_perm [2, 3, 0, 1]
+  x += dpp_mov<0x141>(x);  // row_half_mirror
+  return x;
+}
 
 template <int D, bool TAN>
 __global__ __launch_bounds__(kThreads) void attn_jvp_f32_kernel(KernelParams p) {
@@ -90,54 +110,55 @@ __global__ __launch_bounds__(kThreads) void attn_jvp_f32_kernel(KernelParams p) 
     __syncthreads();
     const uint32_t bits = ent.y >= 0 ? p.partial_bits[int64_t(ent.y) * BM + row_in_tile] : ~0u;
 
-    float s[BN], ds[BN];
-    float mx = kNegInf;
 #pragma unroll
-    for (int j = 0; j < BN; ++j) {
-      float a = 0.f, b = 0.f;
+    for (int h = 0; h < BN / HB; ++h) {
+      float s[HB], ds[HB];
+      float mx = kNegInf;
+#pragma unroll
+      for (int jj = 0; jj < HB; ++jj) {
+        const int j = h * HB + jj;
+        float a = 0.f, b = 0.f;
+#pragma unroll
+        for (int x = 0; x < DS; ++x) {
+          a = fmaf(q[x], Ks[j * LD + d0 + x], a);
+          if (TAN) {
+            b = fmaf(dq[x], Ks[j * LD + d0 + x], b);
+            b = fmaf(q[x], dKs[j * LD + d0 + x], b);
+          }
+        }
+        a = sum8(a);
+        if (TAN) b = sum8(b);
+        const bool ok = (bits >> j) & 1u;
+        s[jj] = ok ? a * p.scale : kNegInf;
+        ds[jj] = ok ? b * p.scale : 0.f;
+        mx = fmaxf(mx, s[jj]);
+      }
+      const float m_new = fmaxf(m_run, mx);
+      const float m_use = m_new == kNegInf ? 0.f : m_new;
+      const float alpha = expf(m_run - m_use);
+      float lsum = 0.f, musum = 0.f;
+#pragma unroll
+      for (int jj = 0; jj < HB; ++jj) {
+        s[jj] = expf(s[jj] - m_use);  // now the weight p_j
+        lsum += s[jj];
+        if (TAN) musum = __builtin_fmaf(s[jj], ds[jj], musum);
+      }
+      l_run = l_run * alpha + lsum;
+      if (TAN) mu_run = mu_run * alpha + musum;
+      m_run = m_new;
 #pragma unroll
       for (int x = 0; x < DS; ++x) {
-        a = fmaf(q[x], Ks[j * LD + d0 + x], a);
-        if (TAN) {
-          b = fmaf(dq[x], Ks[j * LD + d0 + x], b);
-          b = fmaf(q[x], dKs[j * LD + d0 + x], b);
+        float a = acc[x] * alpha, t = tac[x] * alpha;
+#pragma unroll
+        for (int jj = 0; jj < HB; ++jj) {
+          const int j = h * HB + jj;
+          const float vj = Vs[j * LD + d0 + x];
+          a = fmaf(s[jj], vj, a);
+          if (TAN) t = fmaf(s[jj], fmaf(ds[jj], vj, dVs[j * LD + d0 + x]), t);
         }
+        acc[x] = a;
+        tac[x] = t;
       }
-      a += __shfl_xor(a, 1, 64);
-      a += __shfl_xor(a, 2, 64);
-      if (TAN) {
-        b += __shfl_xor(b, 1, 64);
-        b += __shfl_xor(b, 2, 64);
-      }
-      const bool ok = (bits >> j) & 1u;
-      s[j] = ok ? a * p.scale : kNegInf;
-      ds[j] = ok ? b * p.scale : 0.f;
-      mx = fmaxf(mx, s[j]);
-    }
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == kNegInf ? 0.f : m_new;
-    const float alpha = expf(m_run - m_use);
-    float lsum = 0.f, musum = 0.f;
-#pragma unroll
-    for (int j = 0; j < BN; ++j) {
-      s[j] = expf(s[j] - m_use);  // now the weight p_j
-      lsum += s[j];
-      if (TAN) musum = __builtin_fmaf(s[j], ds[j], musum);
-    }
-    l_run = l_run * alpha + lsum;
-    if (TAN) mu_run = mu_run * alpha + musum;
-    m_run = m_new;
-#pragma unroll
-    for (int x = 0; x < DS; ++x) {
-      float a = acc[x] * alpha, t = tac[x] * alpha;
-#pragma unroll
-      for (int j = 0; j < BN; ++j) {
-        const float vj = Vs[j * LD + d0 + x];
-        a = fmaf(s[j], vj, a);
-        if (TAN) t = fmaf(s[j], fmaf(ds[j], vj, dVs[j * LD + d0 + x]), t);
-      }
-      acc[x] = a;
-      tac[x] = t;
     }
   }
 
