@@ -221,15 +221,19 @@ def attn_jvp_fwd(q, k, v, dq, dk, dv, mask, scale=None, o=None, d_o=None, lse=No
     tangent = dq is not None or dk is not None or dv is not None
     if q.dim() != 4 or k.dim() != 4:
         raise ValueError("tensors must be [B, N, H, D]")
-    B, n_q, H, D = q.shape
-    n_k = k.shape[1]
-    for name, t, rows in (("k", k, n_k), ("v", v, n_k), ("dq", dq, n_q), ("dk", dk, n_k),
-                          ("dv", dv, n_k)):
+    qshape, kshape = q.shape, k.shape
+    B, n_q, H, D = qshape
+    n_k = kshape[1]
+    if kshape != (B, n_k, H, D):
+        raise ValueError(f"k has shape {tuple(kshape)}, expected {(B, n_k, H, D)}")
+    qdt, qdev = q.dtype, q.device
+    for name, t, want in (("k", k, kshape), ("v", v, kshape), ("dq", dq, qshape), ("dk", dk, kshape),
+                          ("dv", dv, kshape)):
         if t is None:
             continue
-        if tuple(t.shape) != (B, rows, H, D):
-            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {(B, rows, H, D)}")
-        if t.dtype != q.dtype or t.device != q.device:
+        if t.shape != want:
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(want)}")
+        if t.dtype != qdt or t.device != qdev:
             raise ValueError(f"{name} differs from q in dtype or device")
     if not q.is_cuda:
         raise ValueError("tensors must live on the GPU")
@@ -237,37 +241,35 @@ def attn_jvp_fwd(q, k, v, dq, dk, dv, mask, scale=None, o=None, d_o=None, lse=No
     want_dlse = lse_tangent or d_lse is not None
     if want_dlse and not tangent:
         raise ValueError("the tangent of lse needs at least one input tangent")
+    qs, ks = q.stride(), k.stride()
     if o is None:
-        o = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
+        o = torch.empty_strided(qshape, qs, dtype=qdt, device=qdev)
     if tangent and d_o is None:
-        d_o = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
+        d_o = torch.empty_strided(qshape, qs, dtype=qdt, device=qdev)
     if lse is None:
-        lse = torch.empty((B, H, n_q), dtype=torch.float32, device=q.device)
+        lse = torch.empty((B, H, n_q), dtype=torch.float32, device=qdev)
     if want_dlse and d_lse is None:
-        d_lse = torch.empty((B, H, n_q), dtype=torch.float32, device=q.device)
+        d_lse = torch.empty((B, H, n_q), dtype=torch.float32, device=qdev)
     for name, t in (("dq", dq), ("o", o), ("d_o", d_o)):
-        if t is not None and (tuple(t.shape) != tuple(q.shape) or t.stride() != q.stride()
-                              or t.dtype != q.dtype):
+        if t is not None and (t.shape != qshape or t.stride() != qs or t.dtype != qdt):
             raise ValueError(f"{name} must match q in shape, strides and dtype")
     for name, t in (("v", v), ("dk", dk), ("dv", dv)):
-        if t is not None and t.stride() != k.stride():
+        if t is not None and t.stride() != ks:
             raise ValueError(f"{name} must have the strides of k")
-    if q.stride(3) != 1 or k.stride(3) != 1:
+    if qs[3] != 1 or ks[3] != 1:
         raise ValueError("the last dimension must be contiguous")
     for name, t in (("lse", lse), ("d_lse", d_lse)):
-        if t is not None and (tuple(t.shape) != (B, H, n_q) or t.dtype != torch.float32
+        if t is not None and (t.shape != (B, H, n_q) or t.dtype != torch.float32
                               or not t.is_contiguous()):
             raise ValueError(f"{name} must be a contiguous float32 [B, H, n_q] tensor")
     ptr = lambda t: t.data_ptr() if t is not None else None
-    a = _lib.AttnJvpArgs(
-        dtype=code, B=B, H=H, n_q=n_q, n_k=n_k, D=D,
-        q=ptr(q), k=ptr(k), v=ptr(v), dq=ptr(dq), dk=ptr(dk), dv=ptr(dv),
-        o=ptr(o), d_o=ptr(d_o) if tangent else None, lse=ptr(lse),
-        q_stride_b=q.stride(0), q_stride_n=q.stride(1), q_stride_h=q.stride(2),
-        k_stride_b=k.stride(0), k_stride_n=k.stride(1), k_stride_h=k.stride(2),
-        scale=float(scale) if scale is not None else 0.0, d_lse=ptr(d_lse))
+    a = _lib.AttnJvpArgs(code, B, H, n_q, n_k, D,
+                         q.data_ptr(), k.data_ptr(), v.data_ptr(), ptr(dq), ptr(dk), ptr(dv),
+                         o.data_ptr(), d_o.data_ptr() if tangent else None, lse.data_ptr(),
+                         qs[0], qs[1], qs[2], ks[0], ks[1], ks[2],
+                         float(scale) if scale is not None else 0.0, ptr(d_lse))
     if stream is None:
-        stream = torch.cuda.current_stream(q.device)
+        stream = torch.cuda.current_stream(qdev)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
     L = _lib.lib()
     if max_splits == "auto":
@@ -276,7 +278,12 @@ def attn_jvp_fwd(q, k, v, dq, dk, dv, mask, scale=None, o=None, d_o=None, lse=No
         _check(L.attn_jvp_split_choose(ctypes.byref(a), mask.handle, n_cu, ctypes.byref(chosen)),
                "attn_jvp_split_choose")
         max_splits = chosen.value
-    with torch.cuda.device(q.device):
+    if max_splits == 1 and workspace is None and torch.cuda.current_device() == qdev.index:
+        # the common case: q's device is already current (no device switch)
+        _check(L.attn_jvp_fwd(ctypes.byref(a), mask.handle, ctypes.c_void_p(handle)), "attn_jvp_fwd")
+        return (o, (d_o if tangent else None), lse, d_lse) if want_dlse else \
+            (o, (d_o if tangent else None), lse)
+    with torch.cuda.device(qdev):
         if max_splits == 1 and workspace is None:
             st = L.attn_jvp_fwd(ctypes.byref(a), mask.handle, ctypes.c_void_p(handle))
             _check(st, "attn_jvp_fwd")
@@ -287,8 +294,8 @@ def attn_jvp_fwd(q, k, v, dq, dk, dv, mask, scale=None, o=None, d_o=None, lse=No
                    "attn_jvp_fwd_split_workspace")
             if workspace is None:
                 workspace = torch.empty(max(int(need.value), 16), dtype=torch.uint8,
-                                        device=q.device)
-            if not workspace.is_cuda or workspace.device != q.device:
+                                        device=qdev)
+            if not workspace.is_cuda or workspace.device != qdev:
                 raise ValueError("workspace must live on the device of q")
             nbytes = workspace.numel() * workspace.element_size()
             st = L.attn_jvp_fwd_split(ctypes.byref(a), mask.handle, int(max_splits),
