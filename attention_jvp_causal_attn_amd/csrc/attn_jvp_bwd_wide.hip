@@ -315,8 +315,9 @@ void bwd_dq_wide_kernel(BwdParams p) {
   }
 
   // Per-lane LDS read offsets, held across the key loop (registers allow it
-  // in this pass); the loop below is unrolled by two so that the ring stage
-  // of every read is an immediate offset.
+  // in this pass); the loop below is unrolled by the ring's stage count (two,
+  // three at head dim 128) so that the ring stage of every read is an
+  // immediate offset.
   const int krow = swap_bits23(col);
   const TrLane tl = tr_lane();
   // A block in two halves.  h1: S^T and dP^T - D (MFMAs from the block's K, V
@@ -552,7 +553,7 @@ void bwd_dkv_wide_kernel(BwdParams p) {
   // Per-lane LDS read offsets: held across the key loop at head dim 64; at
   // head dim 128, where registers are short, the row-read offsets are rebuilt
   // per block (one xor-add per read) and only the transposed-read offsets are
-  // held.  The loop is unrolled by two as in the dQ pass.
+  // held.  The loop is unrolled by the stage count as in the dQ pass.
   constexpr bool kHoist = D == 64;
   const int qperm_h = swap_bits23(col);
   const TrLane tl_h = tr_lane();
