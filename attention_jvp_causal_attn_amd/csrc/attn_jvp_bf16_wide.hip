@@ -34,7 +34,9 @@
 //    the block) go HBM -> LDS with direct-to-LDS loads, 16 bytes per lane per
 //    copy, into a 2-stage ring: block j + 1 is copied while block j is
 //    computed; tiles are XOR-swizzled in 16-byte chunks so the operand reads
-//    hit distinct banks;
+//    hit distinct banks.  The head-dim-128 primal-only kernel, which has the
+//    registers for two score tiles, takes blocks of 64 keys, halving the
+//    per-block barrier, copy and schedule work per key;
 //  * head dim 64 runs the same code with half the k-steps and output tiles
 //    (and 128-byte rows: other swizzles, two tensors per copy round);
 //  * every value lives in the 256 VGPRs a wave has at two waves per SIMD
