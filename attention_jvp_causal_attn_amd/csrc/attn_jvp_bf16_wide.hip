@@ -41,8 +41,9 @@
 //    (and 128-byte rows: other swizzles, two tensors per copy round);
 //  * every value lives in the 256 VGPRs a wave has at two waves per SIMD
 //    (accumulators included, so the rare rescale is plain vector code); the
-//    reference max moves only when a row max exceeds it by more than 2^8, so
-//    p = exp2(s - m) stays below 2^8, far inside fp32 and bf16 range;
+//    reference max moves only when a row max exceeds it by more than 2^16, so
+//    p = exp2(s - m) stays below 2^16, far inside fp32 and bf16 range (bf16
+//    keeps 8 significant bits at any magnitude);
 //  * workgroups are mapped to work so that each XCD receives an equal share
 //    of every group of (batch, head) slices, as interleaved heavy-first tile
 //    slots, while the workgroups resident on one XCD at a time belong to the
@@ -73,7 +74,7 @@ static_assert(BM == 32 * kWaves && BN == 32, "one wave per 32 rows, 32-key block
 
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLn2 = 0.69314718055994530942f;
-constexpr float kRescaleSlack = 8.0f;  // log2 units: p <= 2^8 between rescales
+constexpr float kRescaleSlack = 16.0f;  // log2 units: p <= 2^16 between rescales
 constexpr int kEntChunk = 512;        // schedule entries staged in LDS at a time
 
 // Per head dim: 16-byte chunks per row, 16-wide k-steps, 32-wide output tiles.
